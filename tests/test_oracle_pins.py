@@ -1,0 +1,347 @@
+"""Pins for the CPU oracle: each function is checked against something other
+than itself -- brute force on tiny inputs, library routines (numpy stable
+argsort and bincount, float64 matmul, torch's bf16 conversion), exact
+rational rounding, and closed forms -- so that a dropped term, a wrong index
+or a transposed operand anywhere in the oracle fails a test here."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from synth import get_config
+from synth.gen import activations, bf16_bits, bits_to_bf16, expert_weights, routing
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+# ------------------------------------------------------------------ bf16 ---
+
+def _torch_bf16_bits(v: np.ndarray) -> np.ndarray:
+    return bf16_bits(torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16))
+
+
+def _exact_bf16(d: float) -> int:
+    """Nearest bf16 to d by exact rational comparison, ties to even mantissa."""
+    # enumerate the two bf16 neighbours bracketing d: scan bit patterns near
+    # the truncation of d's binary32 encoding
+    f32 = np.float32(d)
+    u = int(np.array([f32], np.float32).view(np.uint32)[0]) >> 16
+    cands = []
+    for b in (u - 1, u, u + 1):
+        b &= 0xFFFF
+        val = np.array([b << 16], np.uint32).view(np.float32)[0]
+        if np.isfinite(val):
+            cands.append((abs(Fraction(float(val)) - Fraction(d)), b))
+    best = min(c[0] for c in cands)
+    ties = [b for dist, b in cands if dist == best]
+    if len(ties) == 1:
+        return ties[0]
+    return [b for b in ties if b % 2 == 0][0]
+
+
+def test_bf16_f32_rounding_matches_torch(orc):
+    rng = np.random.default_rng(123)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-38).astype(np.float32),  # denormals
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.4e38, -3.4e38, np.inf, -np.inf], np.float32),
+    ])
+    # exact ties: bf16 value + half an ulp, both parities of the kept bit
+    base = rng.integers(0x3000, 0x4f00, size=2000).astype(np.uint32)
+    ties = ((base << 16) | 0x8000).view(np.float32)
+    vals = np.concatenate([vals, ties])
+    ours = np.array([orc.f32_to_bf16(float(v)) for v in vals], np.uint16)
+    np.testing.assert_array_equal(ours, _torch_bf16_bits(vals))
+
+
+def test_bf16_f64_rounding_is_exact(orc):
+    rng = np.random.default_rng(7)
+    vals = list(rng.standard_normal(1500) * 10.0 ** rng.integers(-6, 6, 1500))
+    # doubles just above / below / on a bf16 midpoint: the binary32 of these
+    # is exactly the midpoint, which is where double rounding would go wrong
+    for b in rng.integers(0x3800, 0x4800, size=300):
+        mid = float(np.array([(int(b) << 16) | 0x8000], np.uint32).view(np.float32)[0])
+        vals += [mid, mid * (1 + 2.0 ** -40), mid * (1 - 2.0 ** -40), -mid * (1 + 2.0 ** -40)]
+    for d in vals:
+        assert orc.f64_to_bf16(float(d)) == _exact_bf16(float(d)), d
+
+
+# ------------------------------------------------------------------ plan ---
+
+def _brute_plan(idx, E, S):
+    """Definition by brute force: count earlier pairs with the same expert."""
+    T, K = idx.shape
+    eps = E // S
+    flat = [int(v) for v in idx.ravel()]
+    counts = [flat.count(e) for e in range(E)]
+    off = []
+    for e in range(E):
+        s = e // eps
+        off.append(sum(counts[s * eps:e]))
+    pos = np.zeros((T, K), np.int64)
+    for f, e in enumerate(flat):
+        pos.flat[f] = off[e] + sum(1 for g in range(f) if flat[g] == e)
+    tot = [sum(counts[s * eps:(s + 1) * eps]) for s in range(S)]
+    return np.array(counts), np.array(off), np.array(tot), pos
+
+
+@pytest.mark.parametrize("T,K,E,S", [(1, 1, 1, 1), (5, 2, 4, 2), (17, 3, 8, 4),
+                                     (33, 4, 16, 16), (9, 8, 8, 1)])
+def test_plan_brute_force(orc, T, K, E, S):
+    rng = np.random.default_rng(T * 100 + K)
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int32)  # duplicates allowed
+    cap = T * K
+    p = orc.plan(idx, E, S, cap)
+    assert p.status == orc.OK
+    c, o, tot, pos = _brute_plan(idx, E, S)
+    np.testing.assert_array_equal(p.counts, c)
+    np.testing.assert_array_equal(p.expert_off, o)
+    np.testing.assert_array_equal(p.slot_total, tot)
+    np.testing.assert_array_equal(p.pos, pos)
+
+
+def _numpy_plan_check(orc, idx, E, S):
+    T, K = idx.shape
+    eps = E // S
+    cap = max(1, T * K)
+    p = orc.plan(idx, E, S, cap)
+    assert p.status == orc.OK
+    flat = idx.ravel().astype(np.int64)
+    counts = np.bincount(flat, minlength=E)
+    np.testing.assert_array_equal(p.counts, counts)
+    assert p.counts.sum() == T * K
+    # slot order = stable sort of the flat pairs by expert id, restarted at
+    # every slot boundary
+    order = np.argsort(flat, kind="stable")
+    sorted_e = flat[order]
+    for s in range(S):
+        sel = (sorted_e // eps) == s
+        pairs = order[sel]                      # flat ids in slot order
+        assert p.slot_total[s] == pairs.size
+        np.testing.assert_array_equal(p.pos.ravel()[pairs], np.arange(pairs.size))
+    # offsets: first row of each expert inside its slot
+    for e in range(E):
+        s = e // eps
+        assert p.expert_off[e] == counts[s * eps:e].sum()
+
+
+def test_plan_library_routine_random_shapes(orc):
+    rng = np.random.default_rng(2024)
+    for trial in range(60):
+        E = int(rng.choice([1, 2, 8, 64, 256]))
+        S = int(rng.choice([s for s in (1, 2, 4, 8) if E % s == 0]))
+        K = int(rng.integers(1, 9))
+        T = int(rng.integers(0, 301))
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+        _numpy_plan_check(orc, idx, E, S)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "dsv3", "decode", "zipf"])
+def test_plan_invariants_on_configs(orc, name):
+    cfg = get_config(name)
+    idx, _ = routing(cfg)
+    p = orc.plan(idx, cfg.E, cfg.S, cfg.cap)
+    assert p.status == orc.OK
+    _numpy_plan_check(orc, idx, cfg.E, cfg.S)
+    # every (token, k) appears exactly once: pos restricted to a slot is a
+    # bijection onto [0, slot_total)
+    eps = cfg.eps
+    slot = idx // eps
+    for s in range(cfg.S):
+        ps = np.sort(p.pos[slot == s])
+        np.testing.assert_array_equal(ps, np.arange(p.slot_total[s]))
+
+
+def test_plan_errors(orc):
+    idx = np.array([[0, 1], [2, 8]], np.int32)
+    assert orc.plan(idx, 8, 4, 100).status == orc.BAD_EXPERT
+    idx = np.array([[0, -1]], np.int32)
+    assert orc.plan(idx, 8, 4, 100).status == orc.BAD_EXPERT
+    # every token to expert 0 of slot 0, over capacity
+    idx = np.zeros((10, 1), np.int32)
+    assert orc.plan(idx, 8, 4, 9).status == orc.CAPACITY
+    assert orc.plan(idx, 8, 4, 10).status == orc.OK
+
+
+# -------------------------------------------------------------- dispatch ---
+
+def test_dispatch_closed_form(orc):
+    cfg = get_config("tiny")
+    x = bf16_bits(activations(cfg))
+    idx, w = routing(cfg)
+    p = orc.plan(idx, cfg.E, cfg.S, cfg.cap)
+    d = orc.dispatch(x, w, idx, p.pos, cfg.E, cfg.S, cfg.cap)
+    eps = cfg.eps
+    seen = np.zeros((cfg.S, cfg.cap), bool)
+    for t in range(cfg.T):
+        for j in range(cfg.K):
+            e = idx[t, j]
+            s, r = e // eps, p.pos[t, j]
+            np.testing.assert_array_equal(d.disp_x[s, r], x[t])
+            assert d.meta_src[s, r] == t * cfg.K + j
+            assert d.meta_w[s, r] == w[t, j]
+            assert d.meta_e[s, r] == e
+            seen[s, r] = True
+    # rows past each slot's total are untouched
+    for s in range(cfg.S):
+        assert seen[s, :p.slot_total[s]].all() and not seen[s, p.slot_total[s]:].any()
+        assert not d.disp_x[s, p.slot_total[s]:].any()
+    # inside an expert's segment the source pairs strictly increase (stable)
+    for e in range(cfg.E):
+        s, o, n = e // eps, p.expert_off[e], p.counts[e]
+        assert np.all(np.diff(d.meta_src[s, o:o + n]) > 0)
+        assert np.all(d.meta_e[s, o:o + n] == e)
+
+
+# ---------------------------------------------------------------- expert ---
+
+def _f32(bits):
+    return bits_to_bf16(bits).to(torch.float64).numpy()
+
+
+def _numpy_swiglu(X, w13_e, w2_e):
+    """float64 matmuls (library routine) with h and y rounded to bf16 by
+    torch's conversion."""
+    I = w13_e.shape[0] // 2
+    x = _f32(X)
+    g = x @ _f32(w13_e[:I]).T
+    u = x @ _f32(w13_e[I:]).T
+    h = (g / (1.0 + np.exp(-g))) * u
+    hb = torch.from_numpy(h).to(torch.bfloat16).to(torch.float64).numpy()
+    y = hb @ _f32(w2_e).T
+    return bf16_bits(torch.from_numpy(y).to(torch.bfloat16)), hb
+
+
+def _ulp_diff(a, b):
+    ai = a.astype(np.int32)
+    bi = b.astype(np.int32)
+    # bf16 sign-magnitude -> ordered integers
+    ai = np.where(ai & 0x8000, 0x8000 - ai, ai)
+    bi = np.where(bi & 0x8000, 0x8000 - bi, bi)
+    return np.abs(ai - bi)
+
+
+@pytest.mark.parametrize("n,H,I", [(1, 16, 8), (7, 64, 32), (40, 256, 96), (3, 96, 200)])
+def test_swiglu_matches_float64_matmul(orc, n, H, I):
+    g = torch.Generator().manual_seed(n * 1000 + H + I)
+    X = bf16_bits(torch.randn(n, H, generator=g).to(torch.bfloat16))
+    w13 = bf16_bits((torch.randn(2 * I, H, generator=g) * 0.1).to(torch.bfloat16))
+    w2 = bf16_bits((torch.randn(H, I, generator=g) * 0.1).to(torch.bfloat16))
+    Y = orc.swiglu_rows(X, w13, w2, nthreads=3)
+    ref, _ = _numpy_swiglu(X, w13, w2)
+    ud = _ulp_diff(Y, ref)
+    # same definition, different summation order in double: only a value
+    # sitting on a bf16 rounding boundary may land one ulp away
+    assert ud.max() <= 1
+    assert (ud > 0).mean() < 0.02
+    # a transposed or swapped operand would be far off
+    yf, rf = _f32(Y), _f32(ref)
+    assert np.abs(yf - rf).max() <= 1e-2 * np.abs(rf).max() + 1e-30
+
+
+def test_swiglu_gate_up_not_swapped(orc):
+    # gate and up play different roles: silu(g)*u != silu(u)*g
+    H, I = 4, 2
+    X = bf16_bits(torch.tensor([[1.0, 0, 0, 0]]).to(torch.bfloat16))
+    w13 = np.zeros((2 * I, H), np.float32)
+    w13[0, 0], w13[1, 0] = 30.0, -30.0     # gate: g = (30, -30)
+    w13[2, 0], w13[3, 0] = 1.0, 1.0        # up:   u = (1, 1)
+    wd = np.zeros((H, I), np.float32)
+    wd[0, 0] = 1.0
+    wd[1, 1] = 1.0
+    Y = orc.swiglu_rows(X, bf16_bits(torch.from_numpy(w13).to(torch.bfloat16)),
+                        bf16_bits(torch.from_numpy(wd).to(torch.bfloat16)))
+    y = _f32(Y)[0]
+    # silu(30) = 30 to far below bf16 resolution; silu(-30) ~ -2.8e-12
+    assert y[0] == 30.0
+    assert -1e-11 < y[1] < 0.0
+    assert y[2] == 0.0 and y[3] == 0.0
+
+
+def test_swiglu_zero_projections_give_zero(orc):
+    g = torch.Generator().manual_seed(5)
+    H, I, n = 64, 48, 9
+    X = bf16_bits(torch.randn(n, H, generator=g).to(torch.bfloat16))
+    w13 = bf16_bits(torch.randn(2 * I, H, generator=g).to(torch.bfloat16))
+    w2 = bf16_bits(torch.randn(H, I, generator=g).to(torch.bfloat16))
+    for zero_rows in (slice(0, I), slice(I, 2 * I)):  # gate = 0, then up = 0
+        wz = w13.copy()
+        wz[zero_rows] = 0
+        Y = orc.swiglu_rows(X, wz, w2)
+        assert not (Y & 0x7FFF).any()  # +0 or -0 everywhere
+
+
+# --------------------------------------------------------------- combine ---
+
+def test_combine_identity_expert(orc):
+    cfg = get_config("tiny")
+    x = bf16_bits(activations(cfg))
+    idx, w = routing(cfg)
+    p = orc.plan(idx, cfg.E, cfg.S, cfg.cap)
+    d = orc.dispatch(x, w, idx, p.pos, cfg.E, cfg.S, cfg.cap)
+    out = orc.combine_tokens(d.disp_x, w, idx, p.pos, cfg.E, cfg.S)
+    # identity experts: out[t] = (sum_j w[t,j]) * x[t], to one bf16 ulp
+    ref = w.astype(np.float64).sum(1, keepdims=True) * _f32(x)
+    refb = bf16_bits(torch.from_numpy(ref).to(torch.bfloat16))
+    assert _ulp_diff(out, refb).max() <= 1
+
+
+def test_combine_k1_unit_weight_is_copy_and_zero_weight_is_zero(orc):
+    rng = np.random.default_rng(3)
+    T, H, E, S = 50, 32, 4, 2
+    x = bf16_bits(torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16))
+    idx = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    cap = T
+    p = orc.plan(idx, E, S, cap)
+    d = orc.dispatch(x, np.ones((T, 1), np.float32), idx, p.pos, E, S, cap)
+    out = orc.combine_tokens(d.disp_x, np.ones((T, 1), np.float32), idx, p.pos, E, S)
+    np.testing.assert_array_equal(out, x)
+    out0 = orc.combine_tokens(d.disp_x, np.zeros((T, 1), np.float32), idx, p.pos, E, S)
+    assert not (out0 & 0x7FFF).any()
+
+
+def test_combine_weights_follow_columns(orc):
+    # distinct rows and weights per column: a misaligned weight index shows
+    rng = np.random.default_rng(11)
+    T, K, H, E, S = 20, 3, 16, 6, 3
+    src = bf16_bits(torch.from_numpy(rng.standard_normal((S, T * K, H), dtype=np.float32)).to(torch.bfloat16))
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    p = orc.plan(idx, E, S, T * K)
+    out = orc.combine_tokens(src, w, idx, p.pos, E, S)
+    eps = E // S
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(K):
+            ref[t] += float(w[t, j]) * _f32(src[idx[t, j] // eps, p.pos[t, j]])
+    refb = bf16_bits(torch.from_numpy(ref).to(torch.bfloat16))
+    assert _ulp_diff(out, refb).max() <= 1
+    # combine_rows is the same arithmetic on explicit row pointers
+    rows = [src[idx[t, j] // eps, p.pos[t, j]] for t in range(T) for j in range(K)]
+    np.testing.assert_array_equal(orc.combine_rows(rows, w), out)
+
+
+# -------------------------------------------------------------- pipeline ---
+
+def test_tiny_pipeline_brute_force(orc):
+    """End to end on the small config against an independent formulation:
+    per token, per chosen expert, SwiGLU by float64 matmul, weighted sum."""
+    cfg = get_config("tiny")
+    xt = activations(cfg)
+    x = bf16_bits(xt)
+    idx, w = routing(cfg)
+    w13t, w2t = expert_weights(cfg, "cpu")
+    w13, w2 = bf16_bits(w13t), bf16_bits(w2t)
+    r = orc.pipeline(x, w, idx, cfg.E, cfg.S, cfg.cap, w13, w2, nthreads=4)
+    ref = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        for j in range(cfg.K):
+            e = idx[t, j]
+            y, _ = _numpy_swiglu(x[t:t + 1], w13[e], w2[e])
+            ref[t] += float(w[t, j]) * _f32(y)[0]
+    refb = bf16_bits(torch.from_numpy(ref).to(torch.bfloat16))
+    o, rb = _f32(r.out), _f32(refb)
+    assert np.abs(o - rb).max() <= 2e-2 * np.abs(rb).max()
+    assert _ulp_diff(r.out, refb).max() <= 2
