@@ -1,0 +1,70 @@
+// cco_internal.h -- types shared by the host side and the kernels of the
+// cco_moe library.  Not installed; the public interface is include/cco_moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cco {
+
+// Wavefront width of CDNA (gfx950).
+constexpr int kWave = 64;
+// XCDs on one MI355X; workgroups are handed to XCDs round-robin by id, so
+// id % kNumXcd names the XCD (and its L2) a workgroup runs on.
+constexpr int kNumXcd = 8;
+// Limits checked on the host before any launch.
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 32;
+// Plan kernels: one workgroup per chunk of flat (token, k) pairs.
+constexpr int kPlanThreads = 256;
+constexpr int kPlanPerThread = 8;
+constexpr int kPlanChunk = kPlanThreads * kPlanPerThread;
+
+// Everything a kernel needs to address the windows of one MoE layer,
+// passed by value so it lands in kernel-argument space (the device
+// communicator idiom of the MORI CCO Guide, "Concepts").
+struct MoeArgs {
+  char *base;          // heap base
+  uint64_t stride;     // bytes per slot
+  uint64_t off_disp_x; // window offsets inside every slot
+  uint64_t off_meta;
+  uint64_t off_hbuf;
+  uint64_t off_out;
+  int64_t cap;         // rows per slot
+  int32_t K, H, E, S, eps, I;
+  int32_t *pos;        // [max_tokens * K]: receive row of each pair (-1: dropped)
+  int32_t *eid;        // [max_tokens * K]: expert id of each pair (-1: invalid)
+  int32_t *counts;     // [E]
+  int32_t *expert_off; // [E]
+  int32_t *slot_total; // [S]
+  int32_t *status;     // [1]
+  int32_t *hist;       // [plan blocks][E + 1] scratch
+  int32_t *ticket;     // [1] scratch, zero between plans
+};
+
+// Address of byte `off` of window `win_off` in slot `s`:
+// base + s * stride + win_off + off.
+__host__ __device__ inline char *slot_addr(const MoeArgs &a, int s, uint64_t win_off,
+                                          uint64_t off) {
+  return a.base + (uint64_t)s * a.stride + win_off + off;
+}
+
+// Launchers, one per kernel file.  Each returns the hipError_t of its launch.
+hipError_t launch_plan_count(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
+                             int32_t nblk, hipStream_t st);
+hipError_t launch_plan_rank(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
+                            int32_t nblk, hipStream_t st);
+hipError_t launch_dispatch(const MoeArgs &a, const uint16_t *x, const float *w,
+                           const int32_t *idx, int32_t T, hipStream_t st);
+hipError_t launch_combine(const MoeArgs &a, uint64_t src_win, const float *w,
+                          const int32_t *idx, uint16_t *out, int32_t T, hipStream_t st);
+hipError_t launch_copy_in(const MoeArgs &a, int32_t slot, const uint16_t *src,
+                          uint64_t dst_win, hipStream_t st);
+
+// Expert GEMMs.  `num_cus` sizes the persistent grids.
+hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int num_cus,
+                                 hipStream_t st);
+hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int num_cus,
+                              hipStream_t st);
+
+}  // namespace cco

@@ -1,0 +1,137 @@
+// combine.hip -- gather every token's expert rows back from the slots and
+// sum them with the routing weights.
+//
+// "MORI CCO: Next-Generation Collective Communication Object for GPUs",
+// section "Zero-copy MoE dispatch -> expert -> combine", step 3: each rank
+// reads its tokens back from the combine staging buffers of the ranks that
+// own the experts and applies the weights.  Row j of token t sits at
+//   base + slot(idx[t][j]) * stride + src_window + pos[t][j] * (2 * H).
+//
+//   out[t][h] = bf16( fma(w[t][K-1], y_{K-1}[h], ... fma(w[t][0], y_0[h], 0)) )
+// in fp32, in j order, rounded once to nearest even.  One wavefront per
+// token; each lane owns 8 output elements per 16-byte vector and issues the
+// K row loads before it accumulates.  Every output element has one owner:
+// no atomics, the result does not depend on scheduling.
+//
+// copy_in_kernel serves the same section's note: an expert output that is
+// not the staging view is copied into the view first (its row count read on
+// the device, so the host never waits for it).
+#include "cco_internal.h"
+
+namespace cco {
+namespace {
+
+constexpr int kCombineWaves = 4;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x0040u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int KT>
+__global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
+    MoeArgs a, uint64_t src_win, const float *__restrict__ w, const int32_t *__restrict__ idx,
+    uint4 *__restrict__ out, int32_t T) {
+  constexpr int KM = KT > 0 ? KT : kMaxTopk;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * kCombineWaves + wave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;
+  const int nk = KT > 0 ? KT : a.K;
+  const int nvec = a.H / 8;
+  const uint64_t rb = (uint64_t)a.H * 2;
+
+  const uint4 *src[KM];
+  float wj[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    src[j] = nullptr;
+    wj[j] = 0.0f;
+    if (j < nk) {
+      const int f = t * nk + j;
+      const int e = idx[f];
+      const int p = a.pos[f];
+      wj[j] = w[f];
+      if ((unsigned)e < (unsigned)a.E && p >= 0 && (int64_t)p < a.cap)
+        src[j] = (const uint4 *)slot_addr(a, e / a.eps, src_win, (uint64_t)p * rb);
+    }
+  }
+  uint4 *orow = out + (int64_t)t * nvec;
+  for (int v = lane; v < nvec; v += kWave) {
+    uint4 r[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < nk && src[j] != nullptr) r[j] = src[j][v];
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < nk && src[j] != nullptr) {
+        const uint32_t c[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = __builtin_fmaf(wj[j], bf16_lo(c[q]), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(wj[j], bf16_hi(c[q]), acc[2 * q + 1]);
+        }
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    orow[v] = o;
+  }
+}
+
+template <int KT>
+hipError_t launch_k(const MoeArgs &a, uint64_t src_win, const float *w, const int32_t *idx,
+                    uint16_t *out, int32_t T, hipStream_t st) {
+  const int nblk = (T + kCombineWaves - 1) / kCombineWaves;
+  hipLaunchKernelGGL(combine_kernel<KT>, dim3(nblk), dim3(kCombineWaves * kWave), 0, st, a,
+                     src_win, w, idx, (uint4 *)out, T);
+  return hipGetLastError();
+}
+
+// Copy slot_total[slot] rows of `src` into window dst_win of `slot`.
+__global__ __launch_bounds__(256) void copy_in_kernel(MoeArgs a, int32_t slot,
+                                                      const uint4 *__restrict__ src,
+                                                      uint64_t dst_win) {
+  int64_t rows = a.slot_total[slot];
+  if (rows > a.cap) rows = a.cap;
+  const int64_t nvec = rows * (a.H / 8);
+  uint4 *dst = (uint4 *)slot_addr(a, slot, dst_win, 0);
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * blockDim.x)
+    dst[v] = src[v];
+}
+
+}  // namespace
+
+hipError_t launch_combine(const MoeArgs &a, uint64_t src_win, const float *w,
+                          const int32_t *idx, uint16_t *out, int32_t T, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  switch (a.K) {
+    case 1: return launch_k<1>(a, src_win, w, idx, out, T, st);
+    case 2: return launch_k<2>(a, src_win, w, idx, out, T, st);
+    case 4: return launch_k<4>(a, src_win, w, idx, out, T, st);
+    case 6: return launch_k<6>(a, src_win, w, idx, out, T, st);
+    case 8: return launch_k<8>(a, src_win, w, idx, out, T, st);
+    default: return launch_k<0>(a, src_win, w, idx, out, T, st);
+  }
+}
+
+hipError_t launch_copy_in(const MoeArgs &a, int32_t slot, const uint16_t *src, uint64_t dst_win,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(copy_in_kernel, dim3(2048), dim3(256), 0, st, a, slot, (const uint4 *)src,
+                     dst_win);
+  return hipGetLastError();
+}
+
+}  // namespace cco

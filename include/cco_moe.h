@@ -1,0 +1,237 @@
+/*
+ * cco_moe.h -- zero-copy MoE dispatch -> expert -> combine over a symmetric
+ * heap, one MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [blog]  "MORI CCO: Next-Generation Collective Communication Object for
+ *           GPUs" (AMD technical article).
+ *   [guide] "MORI CCO Guide", sections "Concepts", "Memory and Windows",
+ *           "C++ API".
+ *
+ * The symmetric heap is one flat device buffer sliced into equal slots; a
+ * window is carved at the same offset in every slot, so the address of a
+ * window in slot s is  base + s * stride + offset  ([blog] "What is MORI
+ * CCO?").  Slots stand in for ranks: on one GPU every slot is a region of
+ * that GPU's own HBM, and "sending to a peer" is a store at a slot address.
+ *
+ * Conventions (after [guide] "C++ API": status-returning calls with
+ * out-parameters, paired create/destroy, and resources owned by the object
+ * that created them and freed with it):
+ *   - every call returns a cco_status (0 = success) unless stated;
+ *   - argument errors are reported before anything is launched;
+ *   - plan / dispatch / expert / combine are asynchronous on `stream` and
+ *     allocate nothing; they must be issued in that order on one stream for
+ *     the same T and the same idx;
+ *   - errors found on the device (a bad expert id, a slot overflow) go to a
+ *     per-object status word that cco_moe_status reads; the next plan
+ *     recomputes it.  Rows that do not fit are dropped, never written out of
+ *     bounds;
+ *   - one cco_moe may not be used from two host threads at once; separate
+ *     objects are independent.
+ *
+ * Data types: bf16 is passed as uint16_t bit patterns; weights are fp32;
+ * expert ids and sizes int32.  All tensors are dense row-major.
+ *
+ * Expert-to-slot map: experts are split into S contiguous blocks of E/S,
+ * expert e lives in slot e / (E/S).
+ * Row order inside a slot: by ascending expert id, and inside one expert by
+ * the flat pair index t*K + j (a stable counting sort).  One row per
+ * (token, k) pair, duplicates included.
+ */
+#ifndef CCO_MOE_H
+#define CCO_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCO_OK = 0,
+  CCO_INFO_COPIED = 1,         /* combine copied a foreign expert output in */
+  CCO_ERR_INVALID_ARG = -1,    /* bad argument, found on the host */
+  CCO_ERR_OUT_OF_MEMORY = -2,  /* device allocation failed (create calls only) */
+  CCO_ERR_HIP = -3,            /* a HIP runtime call failed */
+  CCO_ERR_CAPACITY = -4,       /* device: a slot received more than cap rows */
+  CCO_ERR_BAD_EXPERT = -5,     /* device: an expert id outside [0, E) */
+  CCO_ERR_HEAP_FULL = -6       /* the heap's slots have no room for this object */
+} cco_status;
+
+/* Opaque handles. */
+typedef struct cco_sym_heap cco_sym_heap;
+typedef struct cco_moe cco_moe;
+
+/* Shape of one MoE layer.
+ *   max_tokens   largest T any call will pass (sizes the receive windows)
+ *   hidden       H, bf16 elements per token row; multiple of 8 (16-byte
+ *                rows); with inter > 0 also a multiple of 128
+ *   topk         K >= 1, experts per token
+ *   num_experts  E >= 1, at most 1024, a multiple of the heap's slot count
+ *   inter        I, SwiGLU intermediate size, a multiple of 64;
+ *                0 selects identity experts (the expert output is the
+ *                dispatched row itself and combine reads the receive window)
+ */
+typedef struct {
+  int32_t max_tokens;
+  int32_t hidden;
+  int32_t topk;
+  int32_t num_experts;
+  int32_t inter;
+} cco_moe_shape;
+
+/* Device pointers of the routing state that plan writes (owned by the
+ * cco_moe; valid until the heap is destroyed). */
+typedef struct {
+  int32_t *pos;        /* [max_tokens][K]: row inside slot(idx[t][j]), -1 if dropped */
+  int32_t *counts;     /* [E]: rows routed to each expert */
+  int32_t *expert_off; /* [E]: first row of each expert inside its slot */
+  int32_t *slot_total; /* [S]: rows received by each slot (the receive count) */
+  int32_t *status;     /* [1]: device status word (0 or a negative cco_status) */
+} cco_moe_routing;
+
+/* Byte offsets of the windows inside every slot (identical in all slots).
+ * A window that the shape does not need has size 0. */
+typedef struct {
+  uint64_t disp_x, disp_x_bytes;       /* dispatched rows  [cap][H] bf16 */
+  uint64_t disp_meta, disp_meta_bytes; /* per-row {src = t*K+j, w, expert} [cap] x 12 B */
+  uint64_t hbuf, hbuf_bytes;           /* SwiGLU intermediate [cap][I] bf16 */
+  uint64_t out_tok, out_tok_bytes;     /* expert output [cap][H] bf16 */
+  int64_t cap;                         /* rows per slot */
+} cco_moe_layout;
+
+/* ---------------------------------------------------------- the heap --- */
+
+/* Create a symmetric heap: ONE device allocation of nslots slots of
+ * `stride` bytes, stride = per_slot_bytes rounded up to 2 MiB, on HIP device
+ * `device`.  [guide] "Memory and Windows": symmetric memory sits at the same
+ * offset on every rank; here every rank is a slot of one buffer.
+ * Errors: CCO_ERR_INVALID_ARG (out == NULL, nslots < 1, per_slot_bytes == 0,
+ * bad device), CCO_ERR_OUT_OF_MEMORY, CCO_ERR_HIP. */
+int cco_sym_heap_create(int device, int32_t nslots, uint64_t per_slot_bytes,
+                        cco_sym_heap **out);
+
+/* Free the heap's buffer and every cco_moe created on it ([guide] "Memory
+ * and Windows": resources are released with their owner).  NULL is a no-op.
+ * Synchronises the device first. */
+int cco_sym_heap_destroy(cco_sym_heap *heap);
+
+/* base + slot * stride + offset ([blog] "What is MORI CCO?", the peer
+ * address formula).  Returns NULL if slot or offset is out of range. */
+void *cco_sym_heap_slot_ptr(const cco_sym_heap *heap, int32_t slot, uint64_t offset);
+
+/* Heap geometry; any out-pointer may be NULL. */
+int cco_sym_heap_info(const cco_sym_heap *heap, void **base, uint64_t *stride,
+                      int32_t *nslots, uint64_t *used);
+
+/* ----------------------------------------------------------- the MoE --- */
+
+/* Bytes of slot space one cco_moe of this shape needs on a heap with nslots
+ * slots (0 if the shape is invalid).  Pure host function. */
+uint64_t cco_moe_required_slot_bytes(const cco_moe_shape *shape, int32_t nslots);
+
+/* Window layout of such an object, relative to its first byte in a slot
+ * (pure host function; CCO_ERR_INVALID_ARG for an invalid shape). */
+int cco_moe_layout_of(const cco_moe_shape *shape, int32_t nslots, cco_moe_layout *out);
+
+/* Carve the windows of one MoE layer out of every slot of `heap`, at the
+ * heap's next free offset (the same in every slot), and allocate its
+ * routing state.  The heap owns the result.  [blog] "Zero-copy MoE
+ * dispatch -> expert -> combine": the op object is built on the
+ * communicator and every intermediate it hands out is a view of symmetric
+ * memory.
+ * Errors: CCO_ERR_INVALID_ARG (shape checks above, E % nslots != 0),
+ * CCO_ERR_HEAP_FULL, CCO_ERR_OUT_OF_MEMORY, CCO_ERR_HIP. */
+int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out);
+
+/* Window offsets of this object inside each slot (absolute, from the slot's
+ * first byte). */
+int cco_moe_get_layout(const cco_moe *m, cco_moe_layout *out);
+
+/* Routing-state device pointers. */
+int cco_moe_get_routing(const cco_moe *m, cco_moe_routing *out);
+
+/* Plan ([blog] "Zero-copy MoE dispatch": dispatch returns the receive count
+ * and a routing object that combine reuses).
+ *   topk_idx  device int32 [T][K], expert ids, row-major, caller-owned
+ *   T         0 <= T <= max_tokens (T == 0 is a no-op that zeroes the counts)
+ * Computes per-expert counts, slot-local expert offsets, per-slot totals and
+ * pos[t][j] = expert_off[e] + number of earlier pairs (flat order t*K+j)
+ * with the same expert e.  Device errors: CCO_ERR_BAD_EXPERT,
+ * CCO_ERR_CAPACITY (reported by cco_moe_status). */
+int cco_moe_plan(cco_moe *m, const int32_t *topk_idx, int32_t T, void *stream);
+
+/* Dispatch ([blog] "Zero-copy MoE dispatch", step 1: each token row is
+ * written straight into the receive window of the slot that owns each of
+ * its experts; no staging copy).
+ *   x        device bf16 [T][H]
+ *   weights  device fp32 [T][K] routing weights (carried into the per-row
+ *            metadata; applied by combine)
+ * For every pair: DISP_X[slot(e)][pos] = x[t] bit for bit and
+ * DISP_META[slot(e)][pos] = {t*K + j, w[t][j], e}.  Needs the same T and
+ * idx as the preceding plan. */
+int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights,
+                     int32_t T, void *stream);
+
+/* Expert ([blog] "Zero-copy MoE dispatch", step 2: the expert reads the
+ * receive window in place and writes the combine staging window, row i to
+ * row i).  SwiGLU per expert e on its rows X of DISP_X:
+ *   h = bf16( silu(X Wg^T) * (X Wu^T) )  -> HBUF  (fp32 accumulation)
+ *   y = bf16( h Wd^T )                   -> OUT_TOK
+ *   w13  device bf16 [E][2I][H]: rows 0..I-1 gate, rows I..2I-1 up
+ *   w2   device bf16 [E][H][I]
+ * (both K-contiguous, like nn.Linear.weight).  Row counts are read on the
+ * device; nothing is copied to the host.  With inter == 0 this is a no-op
+ * (identity experts; w13 and w2 may be NULL). */
+int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *stream);
+
+/* Receive window (recv_x) of `slot`: DISP_X base, [cap][H] bf16; rows
+ * [expert_off[e], expert_off[e] + counts[e]) belong to expert e.  NULL if
+ * slot is out of range. */
+void *cco_moe_dispatch_view(cco_moe *m, int32_t slot);
+
+/* Combine staging window of `slot` ([blog] "Zero-copy MoE dispatch":
+ * combine_in_view): OUT_TOK base, or DISP_X for identity experts. */
+void *cco_moe_combine_in_view(cco_moe *m, int32_t slot);
+
+/* Combine ([blog] "Zero-copy MoE dispatch", step 3: each token reads its
+ * rows back from the slots that own its experts and sums them with its
+ * routing weights).
+ *   expert_out  host array of S device pointers, the expert output of each
+ *               slot ([slot_total][H] bf16, row i for receive row i), or
+ *               NULL to use the staging views.  A slot whose pointer is not
+ *               its staging view is first copied into the view (one device
+ *               copy of its rows) and the call returns CCO_INFO_COPIED
+ *               ([blog] "Zero-copy MoE dispatch", note on the data_ptr
+ *               match).
+ *   weights     device fp32 [T][K]
+ *   out         device bf16 [T][H], caller-owned
+ *   out[t] = bf16( sum_j w[t][j] * y[slot(e)][pos[t][j]] ), fp32 fused
+ *   multiply-add in j = 0..K-1 order, rounded once to nearest even. */
+int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weights,
+                    uint16_t *out, int32_t T, void *stream);
+
+/* Synchronise `stream`, copy the receive counts to the host (either pointer
+ * may be NULL; slot_total is [S], expert_counts is [E]) and return the
+ * device status word (CCO_OK, CCO_ERR_BAD_EXPERT or CCO_ERR_CAPACITY), or
+ * CCO_ERR_HIP. */
+int cco_moe_status(cco_moe *m, void *stream, int32_t *slot_total, int32_t *expert_counts);
+
+/* Per-kernel timing with HIP events on the launch stream.  While enabled,
+ * each kernel launch of this object is bracketed by a pair of events; the
+ * summary returns, per kernel kind, the number of timed launches and their
+ * total milliseconds (kinds: 0 plan-count, 1 plan-rank, 2 dispatch,
+ * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in).
+ * Reading the summary synchronises the recorded events and resets it. */
+#define CCO_NUM_KERNEL_KINDS 7
+int cco_moe_set_timing(cco_moe *m, int enable);
+int cco_moe_timing_summary(cco_moe *m, int32_t *launches, double *total_ms);
+
+/* Human-readable name of a status code (static string). */
+const char *cco_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCO_MOE_H */
