@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the zero-copy MoE dispatch -> expert -> combine path.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+
+One step = the whole path on one batch: plan, dispatch, expert (SwiGLU
+gate/up + down), combine.  Inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.  Prints ONE JSON line:
+whole-step throughput (tokens/s), per-kernel times from HIP events on the
+launch stream, the roofline of the dominant kernel and the CPU oracle timed
+on a bounded sample of the same workload.
+
+This build runs on one GPU: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def stage_work(cfg):
+    """Algorithmic bytes / flops per launch of each kernel (what the method
+    must move or compute; not what a kernel happens to re-read)."""
+    T, H, K, E, I = cfg.T, cfg.H, cfg.K, cfg.E, cfg.I
+    TK = T * K
+    w = {
+        # plan: read idx twice (count, rank), write pos + expert ids, counts/offsets
+        "plan_count": dict(bytes=4 * TK + 12 * E),
+        "plan_rank": dict(bytes=4 * TK + 8 * TK),
+        # dispatch: read x once, write K rows + 12 B metadata, read idx/pos/w
+        "dispatch": dict(bytes=2 * T * H + 2 * TK * H + 24 * TK),
+        # combine: read K rows, write out, read w/idx/pos
+        "combine": dict(bytes=2 * TK * H + 2 * T * H + 12 * TK),
+    }
+    if I > 0:
+        # gate/up: X rows, gate+up weights of the active experts, h out
+        w["expert_gate_up"] = dict(flops=4 * TK * H * I, bytes=2 * TK * H + 4 * E * I * H + 2 * TK * I)
+        # down: h rows, down weights, y out
+        w["expert_down"] = dict(flops=2 * TK * H * I, bytes=2 * TK * I + 2 * E * H * I + 2 * TK * H)
+    return w
+
+
+def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthreads):
+    """The oracle, untuned, on a bounded sample of the same workload; returns
+    a dict in tokens/s."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    eps = cfg.eps
+    t0 = time.perf_counter()
+    pl = orc.plan(idx_np, cfg.E, cfg.S, cfg.cap)
+    t_plan = time.perf_counter() - t0
+    # dispatch and combine on a token sample (the oracle writes full slot
+    # arrays, so its dispatch runs on a sub-batch sized for them)
+    ts = min(cfg.T, 256)
+    sub_idx, sub_w, sub_x = idx_np[:ts], w_np[:ts], x_np[:ts]
+    sub_cap = ts * min(cfg.K, eps)
+    sp = orc.plan(sub_idx, cfg.E, cfg.S, sub_cap)
+    t0 = time.perf_counter()
+    d = orc.dispatch(sub_x, sub_w, sub_idx, sp.pos, cfg.E, cfg.S, sub_cap)
+    t_disp = (time.perf_counter() - t0) / ts
+    t0 = time.perf_counter()
+    orc.combine_tokens(d.disp_x, sub_w, sub_idx, sp.pos, cfg.E, cfg.S)
+    t_comb = (time.perf_counter() - t0) / ts
+    del d
+    # expert: every row of the sampled experts
+    rows = 0
+    t_exp = 0.0
+    if cfg.I > 0:
+        for e, (w13e, w2e) in zip(sample_experts, w13_host):
+            n = int(counts[e])
+            X = x_np[np.nonzero((idx_np == e).any(axis=1))[0][:n]]
+            t0 = time.perf_counter()
+            orc.swiglu_rows(X, w13e, w2e, nthreads)
+            t_exp += time.perf_counter() - t0
+            rows += X.shape[0]
+    per_row = t_exp / rows if rows else 0.0
+    step_s = t_plan + cfg.T * (t_disp + t_comb) + cfg.T * cfg.K * per_row
+    sample = ("plan on all %d (token, k) pairs; dispatch and combine on %d tokens; "
+              "SwiGLU expert on all %d rows of experts %s with %d threads; step time "
+              "extrapolated to %d tokens x %d rows each" %
+              (cfg.T * cfg.K, ts, rows, list(sample_experts), nthreads, cfg.T, cfg.K))
+    return {"value": round(cfg.T / step_s, 3), "unit": "tokens/s", "cores": int(nthreads),
+            "kind": "oracle", "sample": sample,
+            "stage_s": {"plan": round(t_plan, 4), "dispatch_per_token": t_disp,
+                        "combine_per_token": t_comb, "expert_per_row": per_row}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run one plain elementwise copy of 1 GiB "
+                         "(reference kernel for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU's share of the path; "
+              "--gpus %d is not supported (use --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_symmetric_memory_amd as ccm
+    from synth import get_config
+    from synth.gen import activations, bf16_bits, expert_weights, routing
+
+    def log(*a):
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+    cfg = get_config(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log("workload", cfg)
+    xt = activations(cfg)
+    idx_np, w_np = routing(cfg)
+    x = xt.to(dev)
+    idx = torch.from_numpy(idx_np).to(dev)
+    w = torch.from_numpy(w_np).to(dev)
+    w13, w2 = expert_weights(cfg, dev)
+    need = ccm.required_slot_bytes(cfg.T, cfg.H, cfg.K, cfg.E, cfg.I, cfg.S)
+    heap = ccm.SymHeap(cfg.S, need, device=0)
+    moe = ccm.MoE(heap, cfg.T, cfg.H, cfg.K, cfg.E, cfg.I)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    log("heap %.2f GiB, weights %.2f GiB" % (heap.stride * cfg.S / 2**30,
+        0 if w13 is None else (w13.numel() + w2.numel()) * 2 / 2**30))
+
+    def step():
+        moe.plan(idx, stream)
+        moe.dispatch(x, w, stream)
+        moe.expert(w13, w2, stream)
+        moe.combine(w, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    code, slot_total, counts = moe.status()
+    if code != ccm.CCO_OK:
+        raise SystemExit("device status %s" % ccm.status_string(code))
+    log("warmup done")
+
+    # ---- timed region: exactly `steps` steps ----
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+    value = cfg.T * args.steps / wall
+    log("timed %d steps: %.3f ms/step (events %.3f ms/step)" % (args.steps, ms_per_step,
+                                                                  gpu_ms / args.steps))
+
+    # ---- per-kernel durations: HIP events on the launch stream ----
+    moe.set_timing(True)
+    nt = max(3, min(args.steps, 10))
+    for _ in range(nt):
+        step()
+    torch.cuda.synchronize()
+    summ = moe.timing_summary()
+    moe.set_timing(False)
+    work = stage_work(cfg)
+    stages = {}
+    for k, (n, ms) in summ.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        st = {"launches": n, "avg_ms": round(avg, 5)}
+        wk = work.get(k, {})
+        if "bytes" in wk:
+            st["alg_bytes"] = wk["bytes"]
+            st["GB_s"] = round(wk["bytes"] / (avg * 1e-3) / 1e9, 1)
+            st["hbm_frac"] = round(st["GB_s"] / HBM_PEAK_GBS, 4)
+        if "flops" in wk:
+            st["alg_flops"] = wk["flops"]
+            st["TFLOP_s"] = round(wk["flops"] / (avg * 1e-3) / 1e12, 2)
+            st["mfma_frac"] = round(st["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)
+        stages[k] = st
+    log("stages", json.dumps(stages))
+
+    if cfg.I > 0:
+        dom = "expert_gate_up"
+        d = stages[dom]
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": d["TFLOP_s"],
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["mfma_frac"],
+                    "traffic": None,
+                    "hbm_view": {"alg_bytes": d["alg_bytes"], "GB_s": d["GB_s"],
+                                 "frac": d["hbm_frac"]}}
+    else:
+        dom = max(("dispatch", "combine"), key=lambda k: stages[k]["avg_ms"])
+        d = stages[dom]
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": d["hbm_frac"], "traffic": None}
+
+    dc_bytes = stages["dispatch"]["alg_bytes"] + stages["combine"]["alg_bytes"]
+    dc_ms = stages["dispatch"]["avg_ms"] + stages["combine"]["avg_ms"]
+    summary = {"dispatch_combine_GB_s": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
+               "dispatch_combine_hbm_frac": round(dc_bytes / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if cfg.I > 0:
+        fl = work["expert_gate_up"]["flops"] + work["expert_down"]["flops"]
+        ex_ms = stages["expert_gate_up"]["avg_ms"] + stages["expert_down"]["avg_ms"]
+        summary["expert_TFLOP_s"] = round(fl / (ex_ms * 1e-3) / 1e12, 2)
+        summary["expert_mfma_frac"] = round(summary["expert_TFLOP_s"] / BF16_PEAK_TFLOPS, 4)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        sample_experts = []
+        w13_host = []
+        if cfg.I > 0:
+            nz = np.nonzero(counts)[0]
+            order = nz[np.argsort(counts[nz], kind="stable")]
+            # two experts near the median row count
+            mid = len(order) // 2
+            sample_experts = [int(order[mid]), int(order[mid + 1])]
+            w13_host = [(bf16_bits(w13[e]), bf16_bits(w2[e])) for e in sample_experts]
+        from oracle import oracle as orc
+        nthreads = orc.default_threads()
+        cpu = cpu_baseline(cfg, bf16_bits(xt), idx_np, w_np, w13_host, sample_experts, counts,
+                           nthreads)
+        log("cpu baseline", json.dumps(cpu))
+
+    res = {
+        "metric": "dispatch+combine HBM GB/s (% peak); expert GEMM TFLOP/s; tokens/sec",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: T=%d H=%d top-%d E=%d over %d slots, SwiGLU I=%d" %
+                   (cfg.name, cfg.T, cfg.H, cfg.K, cfg.E, cfg.S, cfg.I),
+                   "T": cfg.T, "H": cfg.H, "K": cfg.K, "E": cfg.E, "S": cfg.S, "I": cfg.I,
+                   "seed": cfg.seed},
+        "summary": summary,
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    heap.destroy()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,6 +7,10 @@
 
 namespace cco {
 
+// 16-byte vector of 32-bit lanes as a first-class clang vector (arrays of
+// these stay in registers; HIP's struct-based uint4 does not reliably).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Wavefront width of CDNA (gfx950).
 constexpr int kWave = 64;
 // XCDs on one MI355X; workgroups are handed to XCDs round-robin by id, so

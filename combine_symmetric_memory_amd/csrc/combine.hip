@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 template <int KT>
 __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
     MoeArgs a, uint64_t src_win, const float *__restrict__ w, const int32_t *__restrict__ idx,
-    uint4 *__restrict__ out, int32_t T) {
+    u32x4 *__restrict__ out, int32_t T) {
   constexpr int KM = KT > 0 ? KT : kMaxTopk;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * kCombineWaves + wave;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
   const int nvec = a.H / 8;
   const uint64_t rb = (uint64_t)a.H * 2;
 
-  const uint4 *src[KM];
+  const u32x4 *src[KM];
   float wj[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
@@ -58,12 +58,12 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
       const int p = a.pos[f];
       wj[j] = w[f];
       if ((unsigned)e < (unsigned)a.E && p >= 0 && (int64_t)p < a.cap)
-        src[j] = (const uint4 *)slot_addr(a, e / a.eps, src_win, (uint64_t)p * rb);
+        src[j] = (const u32x4 *)slot_addr(a, e / a.eps, src_win, (uint64_t)p * rb);
     }
   }
-  uint4 *orow = out + (int64_t)t * nvec;
+  u32x4 *orow = out + (int64_t)t * nvec;
   for (int v = lane; v < nvec; v += kWave) {
-    uint4 r[KM];
+    u32x4 r[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (j < nk && src[j] != nullptr) r[j] = src[j][v];
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
         }
       }
     }
-    uint4 o;
+    u32x4 o;
     o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
     o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
     o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
@@ -95,18 +95,18 @@ hipError_t launch_k(const MoeArgs &a, uint64_t src_win, const float *w, const in
                     uint16_t *out, int32_t T, hipStream_t st) {
   const int nblk = (T + kCombineWaves - 1) / kCombineWaves;
   hipLaunchKernelGGL(combine_kernel<KT>, dim3(nblk), dim3(kCombineWaves * kWave), 0, st, a,
-                     src_win, w, idx, (uint4 *)out, T);
+                     src_win, w, idx, (u32x4 *)out, T);
   return hipGetLastError();
 }
 
 // Copy slot_total[slot] rows of `src` into window dst_win of `slot`.
 __global__ __launch_bounds__(256) void copy_in_kernel(MoeArgs a, int32_t slot,
-                                                      const uint4 *__restrict__ src,
+                                                      const u32x4 *__restrict__ src,
                                                       uint64_t dst_win) {
   int64_t rows = a.slot_total[slot];
   if (rows > a.cap) rows = a.cap;
   const int64_t nvec = rows * (a.H / 8);
-  uint4 *dst = (uint4 *)slot_addr(a, slot, dst_win, 0);
+  u32x4 *dst = (u32x4 *)slot_addr(a, slot, dst_win, 0);
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
        v += (int64_t)gridDim.x * blockDim.x)
     dst[v] = src[v];
@@ -129,7 +129,7 @@ hipError_t launch_combine(const MoeArgs &a, uint64_t src_win, const float *w,
 
 hipError_t launch_copy_in(const MoeArgs &a, int32_t slot, const uint16_t *src, uint64_t dst_win,
                           hipStream_t st) {
-  hipLaunchKernelGGL(copy_in_kernel, dim3(2048), dim3(256), 0, st, a, slot, (const uint4 *)src,
+  hipLaunchKernelGGL(copy_in_kernel, dim3(2048), dim3(256), 0, st, a, slot, (const u32x4 *)src,
                      dst_win);
   return hipGetLastError();
 }

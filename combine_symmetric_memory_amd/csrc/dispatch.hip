@@ -26,13 +26,13 @@ struct RowMeta {
 };
 
 template <int KT>
-__device__ __forceinline__ void dispatch_token(const MoeArgs &a, const uint4 *__restrict__ xr,
+__device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__restrict__ xr,
                                                const float *__restrict__ w,
                                                const int32_t *__restrict__ idx, int t, int lane,
                                                int K) {
   constexpr int KM = KT > 0 ? KT : kMaxTopk;
   const int nk = KT > 0 ? KT : K;
-  uint4 *dst[KM];
+  u32x4 *dst[KM];
   const int nvec = a.H / 8;
   const uint64_t rb = (uint64_t)a.H * 2;
 #pragma unroll
@@ -43,13 +43,13 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const uint4 *__
       const int e = idx[f];
       const int p = a.pos[f];
       if ((unsigned)e < (unsigned)a.E && p >= 0 && (int64_t)p < a.cap)
-        dst[j] = (uint4 *)slot_addr(a, e / a.eps, a.off_disp_x, (uint64_t)p * rb);
+        dst[j] = (u32x4 *)slot_addr(a, e / a.eps, a.off_disp_x, (uint64_t)p * rb);
     }
   }
   // four vectors in flight per lane, then the tail one at a time
   int v = lane;
   for (; v + 3 * kWave < nvec; v += 4 * kWave) {
-    const uint4 r0 = xr[v], r1 = xr[v + kWave], r2 = xr[v + 2 * kWave], r3 = xr[v + 3 * kWave];
+    const u32x4 r0 = xr[v], r1 = xr[v + kWave], r2 = xr[v + 2 * kWave], r3 = xr[v + 3 * kWave];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j < nk && dst[j] != nullptr) {
@@ -61,7 +61,7 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const uint4 *__
     }
   }
   for (; v < nvec; v += kWave) {
-    const uint4 r0 = xr[v];
+    const u32x4 r0 = xr[v];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (j < nk && dst[j] != nullptr) dst[j][v] = r0;
@@ -81,13 +81,13 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const uint4 *__
 
 template <int KT>
 __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(
-    MoeArgs a, const uint4 *__restrict__ x, const float *__restrict__ w,
+    MoeArgs a, const u32x4 *__restrict__ x, const float *__restrict__ w,
     const int32_t *__restrict__ idx, int32_t T) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * kDispatchWaves + wave;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
-  const uint4 *xr = x + (int64_t)t * (a.H / 8);
+  const u32x4 *xr = x + (int64_t)t * (a.H / 8);
   dispatch_token<KT>(a, xr, w, idx, t, lane, a.K);
 }
 
@@ -96,7 +96,7 @@ hipError_t launch_k(const MoeArgs &a, const uint16_t *x, const float *w, const i
                     int32_t T, hipStream_t st) {
   const int nblk = (T + kDispatchWaves - 1) / kDispatchWaves;
   hipLaunchKernelGGL(dispatch_kernel<KT>, dim3(nblk), dim3(kDispatchWaves * kWave), 0, st, a,
-                     (const uint4 *)x, w, idx, T);
+                     (const u32x4 *)x, w, idx, T);
   return hipGetLastError();
 }
 

@@ -183,27 +183,29 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    uint4 ra[CA], rb[CB];
+    u32x4 ra[CA], rb[CB];
 #pragma unroll
-    for (int q = 0; q < CA; ++q) ra[q] = *(const uint4 *)pa[q];
+    for (int q = 0; q < CA; ++q) ra[q] = *(const u32x4 *)pa[q];
 #pragma unroll
-    for (int q = 0; q < CB; ++q) rb[q] = *(const uint4 *)pb[q];
+    for (int q = 0; q < CB; ++q) rb[q] = *(const u32x4 *)pb[q];
 #pragma unroll
-    for (int q = 0; q < CA; ++q) *(uint4 *)(smem + la[q]) = ra[q];
+    for (int q = 0; q < CA; ++q) *(u32x4 *)(smem + la[q]) = ra[q];
 #pragma unroll
-    for (int q = 0; q < CB; ++q) *(uint4 *)(smem + lb[q]) = rb[q];
+    for (int q = 0; q < CB; ++q) *(u32x4 *)(smem + lb[q]) = rb[q];
     __syncthreads();
 
     const int nk = g.kdim / BK;
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        const int koff = (kt + 1) * BK;
+      // prefetch the next K-slice; the last step re-reads its own slice so
+      // that the loads are unconditional and the registers never leave VGPRs
+      const int koff = (kt + 1 < nk ? kt + 1 : kt) * BK;
 #pragma unroll
-        for (int q = 0; q < CA; ++q) ra[q] = *(const uint4 *)(pa[q] + koff);
+      for (int q = 0; q < CA; ++q) ra[q] = *(const u32x4 *)(pa[q] + koff);
 #pragma unroll
-        for (int q = 0; q < CB; ++q) rb[q] = *(const uint4 *)(pb[q] + koff);
-      }
+      for (int q = 0; q < CB; ++q) rb[q] = *(const u32x4 *)(pb[q] + koff);
+      // keep the prefetch at the top of the step, ahead of the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
       const uint16_t *sA = smem + cur * STAGE;
       const uint16_t *sB = sA + A_ELEMS;
 #pragma unroll
@@ -222,13 +224,12 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) {
-        uint16_t *dst = smem + (cur ^ 1) * STAGE;
+      // the other buffer was last read before the previous barrier
+      uint16_t *dst = smem + (cur ^ 1) * STAGE;
 #pragma unroll
-        for (int q = 0; q < CA; ++q) *(uint4 *)(dst + la[q]) = ra[q];
+      for (int q = 0; q < CA; ++q) *(u32x4 *)(dst + la[q]) = ra[q];
 #pragma unroll
-        for (int q = 0; q < CB; ++q) *(uint4 *)(dst + lb[q]) = rb[q];
-      }
+      for (int q = 0; q < CB; ++q) *(u32x4 *)(dst + lb[q]) = rb[q];
       __syncthreads();
     }
 
