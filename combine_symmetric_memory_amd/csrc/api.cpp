@@ -85,7 +85,7 @@ bool shape_ok(const cco_moe_shape *s, int32_t nslots) {
   if (s->topk > cco::kMaxTopk || s->num_experts > cco::kMaxExperts) return false;
   if (s->num_experts % nslots != 0) return false;
   if (s->inter < 0) return false;
-  if (s->inter > 0 && (s->inter % 64 != 0 || s->hidden % 128 != 0)) return false;
+  if (s->inter > 0 && (s->inter % 128 != 0 || s->hidden % 256 != 0)) return false;
   // int32 row and pair indices
   const int64_t eps = s->num_experts / nslots;
   const int64_t cap = (int64_t)s->max_tokens * std::min<int64_t>(s->topk, eps);
@@ -269,9 +269,10 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   const int64_t npairs = (int64_t)shape->max_tokens * shape->topk;
   m->max_plan_blocks = plan_blocks(npairs);
   const int E = shape->num_experts;
-  // routing state: pos, eid, counts, expert_off, slot_total, status, ticket, hist
+  // routing state: pos, eid, counts, expert_off, slot_total, status, ticket,
+  // GEMM tile queues, hist
   const size_t n_i32 = (size_t)npairs * 2 + (size_t)E * 2 + (size_t)m->S + 2 +
-                       (size_t)m->max_plan_blocks * (E + 1);
+                       2 * (cco::kNumXcd + 1) + (size_t)m->max_plan_blocks * (E + 1);
   void *st = nullptr;
   hipError_t err = hipMalloc(&st, std::max<size_t>(n_i32, 1) * sizeof(int32_t));
   if (err != hipSuccess) {
@@ -305,6 +306,7 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   a.slot_total = p;        p += m->S;
   a.status = p;            p += 1;
   a.ticket = p;            p += 1;
+  a.gemm_queue = p;        p += 2 * (cco::kNumXcd + 1);
   a.hist = p;
 
   // guard bytes after every window of every slot

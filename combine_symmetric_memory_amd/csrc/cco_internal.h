@@ -44,6 +44,7 @@ struct MoeArgs {
   int32_t *status;     // [1]
   int32_t *hist;       // [plan blocks][E + 1] scratch
   int32_t *ticket;     // [1] scratch, zero between plans
+  int32_t *gemm_queue; // [2][kNumXcd + 1] tile queues of the two expert GEMMs, zero between launches
 };
 
 // Address of byte `off` of window `win_off` in slot `s`:

@@ -26,6 +26,8 @@
 // projections so that each wavefront holds, for the same 32 intermediate
 // columns, the gate accumulator in block 2p and the up accumulator in block
 // 2p+1 with identical lane layouts; the SwiGLU epilogue is elementwise.
+#include <type_traits>
+
 #include "cco_internal.h"
 
 namespace cco {
@@ -53,6 +55,7 @@ struct GemmDesc {
   int32_t kdim;          // reduction length
   int32_t ntiles;        // tiles along N
   int32_t up_off;        // gate/up: first row of the up projection (= I)
+  int32_t *queue;        // [kNumXcd] next-tile counters + [1] exit counter
 };
 
 // Rows of expert e that fit its slot (a slot overflow is reported by the
@@ -64,33 +67,83 @@ __device__ __forceinline__ int rows_of(const MoeArgs &a, int e) {
   return n > 0 ? (int)n : 0;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
-  constexpr int NT = WM * WN * kWave;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int LDS_STRIDE = BK + 8;  // elements; 16-byte pad per row
-  constexpr int A_ELEMS = BM * LDS_STRIDE;
-  constexpr int B_ELEMS = BN * LDS_STRIDE;
-  constexpr int STAGE = A_ELEMS + B_ELEMS;
-  constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
-  constexpr int CA = BM * CPR / NT;
-  constexpr int CB = BN * CPR / NT;
-  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/threads mismatch");
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-  static_assert(!SWIGLU || FN % 2 == 0, "gate/up pairs need an even block count");
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (the direct-to-LDS loads included).
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8), issued through the builtin so that the
+// compiler's own wait insertion sees them.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-  extern __shared__ __align__(16) uint16_t smem[];
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// waits for every outstanding load, prefetches of later stages included.
+// Callers order their own LDS traffic with explicit vmcnt waits.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// One 16-byte-per-lane direct load from global memory into LDS: lane l's
+// 16 bytes land at lds_base + 16 * l (lds_base is wavefront-uniform).
+__device__ __forceinline__ void load_lds_16(const void *gptr, char *lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t *)gptr, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// LDS tile layout: rows of BK bf16 (ROWB bytes), unpadded, 16-byte chunks
+// XOR-swizzled per row so that the 16 rows one fragment read touches fall
+// on distinct bank groups: physical chunk = logical chunk ^ swz(row).
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  return (row / (16 / CPR)) % CPR;
+}
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool SWIGLU>
+__global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
+  constexpr int NW = WM * WN;          // wavefronts per workgroup (one per SIMD)
+  constexpr int NT = NW * kWave;
+  constexpr int TN = BN / WN;          // columns per wavefront
+  constexpr int FN = TN / 32;          // 32-column blocks per wavefront
+  constexpr int MB = BM / 32;          // 32-row blocks per tile
+  constexpr int FM = MB / WM;          // 32-row blocks per wavefront (interleaved)
+  constexpr int ROWB = BK * 2;         // bytes per LDS row
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;     // rows filled by one 1 KiB wavefront load
+  constexpr int A_BYTES = BM * ROWB;
+  constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  constexpr int LA = BM / (RPI * NW);  // A loads per wavefront per K-step
+  constexpr int LB = BN / (RPI * NW);  // B loads per wavefront per K-step
+  constexpr int KSUB = BK / 16;        // MFMA sub-steps per K-step
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
+  static_assert(MB % WM == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
+  static_assert(!SWIGLU || FN % 2 == 0, "gate/up pairs need an even block count");
+  static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
+  static_assert(STAGES >= 2 && (STAGES - 2) * (LA + LB) < 64, "vmcnt range");
+
+  extern __shared__ __align__(1024) char smem[];  // STAGES stages of A and B tiles
   __shared__ int32_t tile_prefix[kMaxExperts + 1];
-  __shared__ int32_t scan_tmp[NT / kWave];
+  __shared__ int32_t scan_tmp[NW];
+  __shared__ int32_t next_tile;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
   const int E = a.E;
 
-  // m-tiles per expert -> exclusive prefix (serial per wavefront chunk)
+  // m-tiles per expert -> exclusive prefix over experts
   {
     constexpr int PER = (kMaxExperts + NT - 1) / NT;
     int32_t loc[PER];
@@ -123,12 +176,25 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
 
   const int ntl = g.ntiles;
   const int total = tile_prefix[E] * ntl;
-  const int nwg_x = gridDim.x / kNumXcd;
+  // tiles are split into kNumXcd contiguous ranges; the workgroups of XCD x
+  // (block id % kNumXcd, the hardware's round-robin placement) take the
+  // tiles of range x in order from a counter, so the tiles running at once
+  // on one XCD are neighbours and share weight panels and receive rows in
+  // that XCD's L2
   const int xcd = blockIdx.x % kNumXcd;
-  const int li = blockIdx.x / kNumXcd;
+  const int t_begin = (int)((int64_t)total * xcd / kNumXcd);
   const int t_end = (int)((int64_t)total * (xcd + 1) / kNumXcd);
 
-  for (int L = (int)((int64_t)total * xcd / kNumXcd) + li; L < t_end; L += nwg_x) {
+  // per-lane position inside a 1 KiB load
+  const int ld_row = lane / CPR;
+  const int ld_pchunk = lane % CPR;
+
+  for (;;) {
+    if (tid == 0) next_tile = t_begin + atomicAdd(&g.queue[xcd], 1);
+    __syncthreads();
+    const int L = next_tile;
+    if (L >= t_end) break;
+
     // decode (expert, n-tile, m-tile): expert e owns [prefix[e], prefix[e+1]) * ntl
     int lo = 0, hi = E;
     while (hi - lo > 1) {
@@ -145,35 +211,54 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
     const int slot = e / a.eps;
     const int64_t grow0 = (int64_t)a.expert_off[e] + row0;
 
-    const uint16_t *A = (const uint16_t *)slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2);
-    const uint16_t *B = g.w + (int64_t)e * g.w_estride;
+    const char *A = slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2);
+    const int nk = g.kdim / BK;
+    const char *B = (const char *)(g.w + (int64_t)e * g.w_estride);
 
-    const uint16_t *pa[CA];
-    const uint16_t *pb[CB];
-    int la[CA], lb[CB];
+    // byte offset (at k = 0) of the chunk each lane loads, from A or B; rows
+    // past the expert's last row re-read that row (a fully idle 32-row
+    // block costs one cache line per load and keeps the loads unconditional)
+    uint32_t oa[LA], ob[LB];
 #pragma unroll
-    for (int q = 0; q < CA; ++q) {
-      const int c = tid + q * NT;
-      const int row = c / CPR, kc = c % CPR;
+    for (int q = 0; q < LA; ++q) {
+      const int row = (q * NW + wave) * RPI + ld_row;
       const int rr = row < rows_valid ? row : rows_valid - 1;
-      pa[q] = A + (int64_t)rr * g.lda + kc * 8;
-      la[q] = row * LDS_STRIDE + kc * 8;
+      oa[q] = (uint32_t)rr * (uint32_t)g.lda * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
     }
 #pragma unroll
-    for (int q = 0; q < CB; ++q) {
-      const int c = tid + q * NT;
-      const int row = c / CPR, kc = c % CPR;
-      int64_t grow;
+    for (int q = 0; q < LB; ++q) {
+      const int row = (q * NW + wave) * RPI + ld_row;
+      uint32_t grow;
       if (SWIGLU) {
         const int wnb = row / TN, jb = (row % TN) / 32, sub = row % 32;
         const int i = n_tile * (BN / 2) + wnb * (TN / 2) + (jb >> 1) * 32 + sub;
-        grow = (jb & 1) ? (int64_t)g.up_off + i : (int64_t)i;
+        grow = (jb & 1) ? (uint32_t)(g.up_off + i) : (uint32_t)i;
       } else {
-        grow = (int64_t)n_tile * BN + row;
+        grow = (uint32_t)(n_tile * BN + row);
       }
-      pb[q] = B + grow * g.ldb + kc * 8;
-      lb[q] = A_ELEMS + row * LDS_STRIDE + kc * 8;
+      ob[q] = grow * (uint32_t)g.ldb * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
     }
+    // Tiles that share a weight panel (same n-tile) or receive rows (same
+    // m-tile) run side by side on one XCD.  In lockstep they would miss the
+    // same L2 lines at the same moment and each fetch them; rotating the K
+    // order by a small tile-dependent lag lets one of them fetch a K-slice
+    // and the others find it in L2 a few K-steps later.  Sharers always get
+    // distinct lags (n-tile % 8 differs for m-tile sharers, m-tile % 4 for
+    // n-tile sharers), and the lag window stays far below the L2 size.
+    const int lag = (n_tile % 8 + m_tile % 4) % nk;
+    // the loads of K-step kt (the tail re-loads the last one) into its stage
+    auto issue_stage = [&](int kt) __attribute__((always_inline)) {
+      int kc = (kt < nk ? kt : nk - 1) + lag;
+      if (kc >= nk) kc -= nk;
+      char *sbase = smem + (kt % STAGES) * STAGE_BYTES;
+      const char *Ak = A + (int64_t)kc * ROWB;
+      const char *Bk = B + (int64_t)kc * ROWB;
+#pragma unroll
+      for (int q = 0; q < LA; ++q) load_lds_16(Ak + oa[q], sbase + (q * NW + wave) * 1024);
+#pragma unroll
+      for (int q = 0; q < LB; ++q)
+        load_lds_16(Bk + ob[q], sbase + A_BYTES + (q * NW + wave) * 1024);
+    };
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -182,69 +267,121 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // this wavefront's blocks (wm + i * WM) holding rows: a prefix i < nact
+    const int mblocks = (rows_valid + 31) / 32;
+    const int nact = min(FM, max(0, (mblocks - wm + WM - 1) / WM));
 
-    u32x4 ra[CA], rb[CB];
+    // the K loop for a wavefront with NACT active 32-row blocks (branch free)
+    //
+    // Software pipeline: the barrier of K-step kt sits before its last
+    // sub-step, so that the first fragments of K-step kt+1 are read while
+    // that sub-step's MFMAs run, and the loads for K-step kt+STAGES are
+    // issued right after it into the stage K-step kt has just finished
+    // reading.  Every K-step issues one stage of loads (the tail re-loads
+    // the last slice), so "stage kt+1 landed" is always vmcnt((STAGES-2) x
+    // loads per stage).
+    auto k_loop = [&](auto nact_c) __attribute__((always_inline)) {
+      constexpr int NACT = decltype(nact_c)::value;
+      constexpr int NF = NACT > 0 ? NACT : 1;
+      constexpr int LPS = LA + LB;
+      static_assert(KSUB % 2 == 0, "fragment buffers alternate across K-steps");
+      bf16x8 fa[2][NF], fb[2][FN];
+      auto read_frags = [&](int stage, int kk, int buf) __attribute__((always_inline)) {
+        const char *sA = smem + stage * STAGE_BYTES;
+        const char *sB = sA + A_BYTES;
+        const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int q = 0; q < CA; ++q) ra[q] = *(const u32x4 *)pa[q];
+        for (int i = 0; i < NACT; ++i) {
+          const int row = (wm + i * WM) * 32 + (lane & 31);
+          fa[buf][i] = *(const bf16x8 *)(sA + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
+        }
 #pragma unroll
-    for (int q = 0; q < CB; ++q) rb[q] = *(const u32x4 *)pb[q];
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * TN + j * 32 + (lane & 31);
+          fb[buf][j] = *(const bf16x8 *)(sB + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
+        }
+      };
+      auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < CA; ++q) *(u32x4 *)(smem + la[q]) = ra[q];
-#pragma unroll
-    for (int q = 0; q < CB; ++q) *(u32x4 *)(smem + lb[q]) = rb[q];
-    __syncthreads();
-
-    const int nk = g.kdim / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      // prefetch the next K-slice; the last step re-reads its own slice so
-      // that the loads are unconditional and the registers never leave VGPRs
-      const int koff = (kt + 1 < nk ? kt + 1 : kt) * BK;
-#pragma unroll
-      for (int q = 0; q < CA; ++q) ra[q] = *(const u32x4 *)(pa[q] + koff);
-#pragma unroll
-      for (int q = 0; q < CB; ++q) rb[q] = *(const u32x4 *)(pb[q] + koff);
-      // keep the prefetch at the top of the step, ahead of the MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t *sA = smem + cur * STAGE;
-      const uint16_t *sB = sA + A_ELEMS;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int kofs = kk * 16 + (lane / 32) * 8;
-        bf16x8 fa[FM], fb[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          fa[i] = *(const bf16x8 *)(sA + (wm * TM + i * 32 + (lane & 31)) * LDS_STRIDE + kofs);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[j] = *(const bf16x8 *)(sB + (wn * TN + j * 32 + (lane & 31)) * LDS_STRIDE + kofs);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < NACT; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
+                                                                0, 0, 0);
+      };
+      constexpr int NMF = NACT * FN;  // MFMAs per sub-step
+      constexpr int NRD = NACT + FN;  // fragment reads per sub-step
+      // prologue: K-steps 0 .. STAGES-1 in flight, K-step 0's first fragments read
+#pragma unroll
+      for (int p = 0; p < STAGES - 1; ++p) issue_stage(p);
+      wait_vmcnt<(STAGES - 2) * LPS>();
+      stage_barrier();
+      issue_stage(STAGES - 1);
+      if (NACT > 0) read_frags(0, 0, 0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt % STAGES;
+#pragma unroll
+        for (int s = 0; s + 1 < KSUB; ++s) {
+          if (NACT > 0) read_frags(cur, s + 1, (s + 1) & 1);
+          mfmas(s & 1);
+        }
+        if (NACT > 0) {
+          // reads of the next sub-step between this sub-step's MFMAs
+#pragma unroll
+          for (int s = 0; s + 1 < KSUB; ++s)
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+              __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+              if (q < NRD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+        }
+        // K-step kt+1 has landed (this wavefront's part) and this
+        // wavefront's reads of K-step kt are done; after the barrier every
+        // part is visible and stage `cur` is free for K-step kt+STAGES
+        wait_vmcnt<(STAGES - 2) * LPS>();
+        wait_lgkmcnt0();
+        stage_barrier();
+        issue_stage(kt + STAGES);
+        if (NACT > 0) read_frags((kt + 1) % STAGES, 0, 0);
+        mfmas((KSUB - 1) & 1);
+        if (NACT > 0) {
+          // the next K-step's first reads, then this stage's loads, between
+          // the last sub-step's MFMAs
+#pragma unroll
+          for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            else if (q < NRD + LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+          }
+        }
       }
-      // the other buffer was last read before the previous barrier
-      uint16_t *dst = smem + (cur ^ 1) * STAGE;
-#pragma unroll
-      for (int q = 0; q < CA; ++q) *(u32x4 *)(dst + la[q]) = ra[q];
-#pragma unroll
-      for (int q = 0; q < CB; ++q) *(u32x4 *)(dst + lb[q]) = rb[q];
-      __syncthreads();
+      wait_vmcnt<0>();  // the tail's re-loads land before the stages are reused
+    };
+    static_assert(FM == 4, "k_loop dispatch below is written for four blocks per wavefront");
+    switch (nact) {
+      case 4: k_loop(std::integral_constant<int, 4>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      case 1: k_loop(std::integral_constant<int, 1>{}); break;
+      default: k_loop(std::integral_constant<int, 0>{}); break;
     }
+    // every wavefront is done with the LDS before the next tile refills it
+    __syncthreads();
 
     // epilogue: lane holds column (lane % 32) of each 32x32 block, rows
     // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v
     uint16_t *C = (uint16_t *)slot_addr(a, slot, g.c_win, (uint64_t)grow0 * g.ldc * 2);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if (i >= nact) continue;
+      const int rb = (wm + i * WM) * 32;
       if (SWIGLU) {
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p) {
           const int col = n_tile * (BN / 2) + wn * (TN / 2) + p * 32 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = wm * TM + i * 32 + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
             if (row < rows_valid) {
               const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
               C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(h);
@@ -257,25 +394,29 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
           const int col = n_tile * BN + wn * TN + j * 32 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = wm * TM + i * 32 + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
             if (row < rows_valid) C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(acc[i][j][v]);
           }
         }
       }
     }
   }
+  // the last workgroup out has seen every counter exhausted: rearm them for
+  // the next launch (ordered by the stream)
+  if (tid == 0 && atomicAdd(&g.queue[kNumXcd], 1) == (int)gridDim.x - 1) {
+#pragma unroll
+    for (int q = 0; q <= kNumXcd; ++q) g.queue[q] = 0;
+  }
 }
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kWM = 2, kWN = 2;
-constexpr int kGemmOccupancy = 2;  // workgroups per CU (LDS: 2 x 72 KiB)
+constexpr int kBM = 256, kBN = 256, kBK = 32, kWM = 2, kWN = 2, kStages = 4;
+constexpr size_t kGemmLds = kStages * (size_t)(kBM + kBN) * kBK * 2;
 
 template <bool SWIGLU>
 hipError_t launch_gemm(const MoeArgs &a, const GemmDesc &g, int num_cus, hipStream_t st) {
-  constexpr size_t lds = 2 * (size_t)(kBM + kBN) * (kBK + 8) * sizeof(uint16_t);
-  int nwg = num_cus * kGemmOccupancy;
-  nwg = ((nwg + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  auto kern = grouped_gemm_kernel<kBM, kBN, kBK, kWM, kWN, SWIGLU>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kWM * kWN * kWave), lds, st, a, g);
+  int nwg = ((num_cus + kNumXcd - 1) / kNumXcd) * kNumXcd;  // one workgroup per CU
+  auto kern = grouped_gemm_kernel<kBM, kBN, kBK, kWM, kWN, kStages, SWIGLU>;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kWM * kWN * kWave), kGemmLds, st, a, g);
   return hipGetLastError();
 }
 
@@ -294,6 +435,7 @@ hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int num_
   g.kdim = a.H;
   g.ntiles = a.I / (kBN / 2);
   g.up_off = a.I;
+  g.queue = a.gemm_queue;
   return launch_gemm<true>(a, g, num_cus, st);
 }
 
@@ -310,6 +452,7 @@ hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int num_cus,
   g.kdim = a.I;
   g.ntiles = a.H / kBN;
   g.up_off = 0;
+  g.queue = a.gemm_queue + kNumXcd + 1;
   return launch_gemm<false>(a, g, num_cus, st);
 }
 

@@ -65,10 +65,10 @@ typedef struct cco_moe cco_moe;
 /* Shape of one MoE layer.
  *   max_tokens   largest T any call will pass (sizes the receive windows)
  *   hidden       H, bf16 elements per token row; multiple of 8 (16-byte
- *                rows); with inter > 0 also a multiple of 128
+ *                rows); with inter > 0 also a multiple of 256
  *   topk         K >= 1, experts per token
  *   num_experts  E >= 1, at most 1024, a multiple of the heap's slot count
- *   inter        I, SwiGLU intermediate size, a multiple of 64;
+ *   inter        I, SwiGLU intermediate size, a multiple of 128;
  *                0 selects identity experts (the expert output is the
  *                dispatched row itself and combine reads the receive window)
  */

@@ -84,8 +84,10 @@ def test_required_bytes_and_layout(capi):
     (dict(K=0), 4),
     (dict(K=33), 4),              # K above the limit
     (dict(E=2048), 4),            # E above the limit
-    (dict(I=100), 4),             # I % 64
-    (dict(H=264, I=512), 4),      # H % 128 with SwiGLU experts
+    (dict(I=100), 4),             # I % 128
+    (dict(I=192), 4),             # I % 128
+    (dict(H=264, I=512), 4),      # H % 256 with SwiGLU experts
+    (dict(H=384, I=512), 4),      # H % 256 with SwiGLU experts
     (dict(T=-1), 4),
     (dict(), 0),
 ])
