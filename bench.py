@@ -50,6 +50,24 @@ def stage_work(cfg):
     return w
 
 
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none for this workload or the expert kernel
+    source changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "traffic_%s.md" % workload)
+    src = os.path.join(ROOT, "combine_symmetric_memory_amd", "csrc", "expert.hip")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"expert_source_sha256: ([0-9a-f]+)", text)
+    if not m or m.group(1) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    m = re.search(r"traffic_bytes_per_launch %s: (\d+)" % re.escape(kernel), text)
+    return int(m.group(1)) if m else None
+
+
 def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthreads):
     """The oracle, untuned, on a bounded sample of the same workload; returns
     a dict in tokens/s."""
@@ -203,14 +221,14 @@ def main():
         d = stages[dom]
         roofline = {"kernel": dom, "bound": "mfma", "achieved": d["TFLOP_s"],
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["mfma_frac"],
-                    "traffic": None,
+                    "traffic": profiled_traffic(cfg.name, dom),
                     "hbm_view": {"alg_bytes": d["alg_bytes"], "GB_s": d["GB_s"],
                                  "frac": d["hbm_frac"]}}
     else:
         dom = max(("dispatch", "combine"), key=lambda k: stages[k]["avg_ms"])
         d = stages[dom]
         roofline = {"kernel": dom, "bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": d["hbm_frac"], "traffic": None}
+                    "unit": "GB/s", "frac": d["hbm_frac"], "traffic": profiled_traffic(cfg.name, dom)}
 
     dc_bytes = stages["dispatch"]["alg_bytes"] + stages["combine"]["alg_bytes"]
     dc_ms = stages["dispatch"]["avg_ms"] + stages["combine"]["avg_ms"]
