@@ -27,6 +27,7 @@
 // columns, the gate accumulator in block 2p and the up accumulator in block
 // 2p+1 with identical lane layouts; the SwiGLU epilogue is elementwise.
 #include <type_traits>
+#include <utility>
 
 #include "cco_internal.h"
 
@@ -105,34 +106,60 @@ __device__ __forceinline__ int swz(int row) {
   return (row / (16 / CPR)) % CPR;
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time
+// indices for register arrays).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool SWIGLU>
-__global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
-  constexpr int NW = WM * WN;          // wavefronts per workgroup (one per SIMD)
+// Tile: BM rows x BN columns of one expert on 8 wavefronts, two per SIMD,
+// in a ping-pong schedule.  Wavefront (g, s) -- group g = wave / 4, SIMD
+// s = wave % 4 -- owns the 32-row blocks g, g+2, g+4, g+6 (interleaved, so
+// a half-empty tile still splits evenly) and columns [s*64, s*64+64), as
+// 32x32 blocks of v_mfma_f32_32x32x16_bf16.
+//
+// Both operands go global -> LDS through a STAGES-deep ring of direct
+// 16-byte-per-lane loads (XOR-swizzled rows, free of bank conflicts).  Time
+// is cut into phases by workgroup barriers; in every phase one group runs
+// only MFMAs on fragments already in registers while the other issues its
+// share of a later stage's loads and reads its next fragments from LDS.
+// Group 1 starts one barrier late, so the two wavefronts of a SIMD always
+// sit in opposite phases and the matrix core never waits for memory.
+template <int BM, int BN, int BK, int STAGES, bool SWIGLU>
+__global__ __launch_bounds__(8 * kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
+  constexpr int NW = 8;
   constexpr int NT = NW * kWave;
-  constexpr int TN = BN / WN;          // columns per wavefront
-  constexpr int FN = TN / 32;          // 32-column blocks per wavefront
-  constexpr int MB = BM / 32;          // 32-row blocks per tile
-  constexpr int FM = MB / WM;          // 32-row blocks per wavefront (interleaved)
-  constexpr int ROWB = BK * 2;         // bytes per LDS row
-  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
-  constexpr int RPI = 1024 / ROWB;     // rows filled by one 1 KiB wavefront load
+  constexpr int WM = 2, WN = 4;
+  constexpr int TN = BN / WN;           // columns per wavefront
+  constexpr int FN = TN / 32;           // 32-column blocks per wavefront
+  constexpr int MB = BM / 32;           // 32-row blocks per tile
+  constexpr int FM = MB / WM;           // 32-row blocks per wavefront
+  constexpr int ROWB = BK * 2;          // bytes per LDS row
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;      // rows filled by one 1 KiB wavefront load
   constexpr int A_BYTES = BM * ROWB;
   constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-  constexpr int LA = BM / (RPI * NW);  // A loads per wavefront per K-step
-  constexpr int LB = BN / (RPI * NW);  // B loads per wavefront per K-step
-  constexpr int KSUB = BK / 16;        // MFMA sub-steps per K-step
+  constexpr int LA = BM / (RPI * NW);   // A loads per wavefront per stage
+  constexpr int LB = BN / (RPI * NW);   // B loads per wavefront per stage
+  constexpr int LPS = LA + LB;
+  constexpr int KSUB = BK / 16;         // MFMA sub-steps per K-step
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
-  static_assert(MB % WM == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-  static_assert(!SWIGLU || FN % 2 == 0, "gate/up pairs need an even block count");
+  static_assert(!SWIGLU || FN == 2, "gate/up: one gate and one up block per wavefront");
   static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
-  static_assert(STAGES >= 2 && (STAGES - 2) * (LA + LB) < 64, "vmcnt range");
+  static_assert(STAGES >= 3 && (STAGES - 2) * LPS < 64, "stage count / vmcnt range");
+  static_assert(FM == 4, "the active-block dispatch below is written for 4 row blocks");
 
-  extern __shared__ __align__(1024) char smem[];  // STAGES stages of A and B tiles
+  extern __shared__ __align__(1024) char smem[];  // STAGES stages of A and B
   __shared__ int32_t tile_prefix[kMaxExperts + 1];
   __shared__ int32_t scan_tmp[NW];
   __shared__ int32_t next_tile;
@@ -140,7 +167,8 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave / WN, wn = wave % WN;
+  const int grp = wave / WN;   // ping-pong group == row half
+  const int wn = wave % WN;    // SIMD == column quarter
   const int E = a.E;
 
   // m-tiles per expert -> exclusive prefix over experts
@@ -210,14 +238,13 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
     const int rows_valid = min(BM, rows_of(a, e) - row0);
     const int slot = e / a.eps;
     const int64_t grow0 = (int64_t)a.expert_off[e] + row0;
+    const int nk = g.kdim / BK;
 
     const char *A = slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2);
-    const int nk = g.kdim / BK;
     const char *B = (const char *)(g.w + (int64_t)e * g.w_estride);
 
-    // byte offset (at k = 0) of the chunk each lane loads, from A or B; rows
-    // past the expert's last row re-read that row (a fully idle 32-row
-    // block costs one cache line per load and keeps the loads unconditional)
+    // byte offset (at k = 0) of the chunk each lane loads; rows past the
+    // expert's last row re-read that row, so the load count never varies
     uint32_t oa[LA], ob[LB];
 #pragma unroll
     for (int q = 0; q < LA; ++q) {
@@ -231,22 +258,19 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
       uint32_t grow;
       if (SWIGLU) {
         const int wnb = row / TN, jb = (row % TN) / 32, sub = row % 32;
-        const int i = n_tile * (BN / 2) + wnb * (TN / 2) + (jb >> 1) * 32 + sub;
-        grow = (jb & 1) ? (uint32_t)(g.up_off + i) : (uint32_t)i;
+        const int i = n_tile * (BN / 2) + wnb * (TN / 2) + sub;
+        grow = jb ? (uint32_t)(g.up_off + i) : (uint32_t)i;
       } else {
         grow = (uint32_t)(n_tile * BN + row);
       }
       ob[q] = grow * (uint32_t)g.ldb * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
     }
-    // Tiles that share a weight panel (same n-tile) or receive rows (same
-    // m-tile) run side by side on one XCD.  In lockstep they would miss the
-    // same L2 lines at the same moment and each fetch them; rotating the K
-    // order by a small tile-dependent lag lets one of them fetch a K-slice
-    // and the others find it in L2 a few K-steps later.  Sharers always get
-    // distinct lags (n-tile % 8 differs for m-tile sharers, m-tile % 4 for
-    // n-tile sharers), and the lag window stays far below the L2 size.
+    // Tiles sharing a weight panel or receive rows run side by side on one
+    // XCD; rotating the K order by a small tile-dependent lag keeps them from
+    // missing the same L2 lines at the same moment.
     const int lag = (n_tile % 8 + m_tile % 4) % nk;
-    // the loads of K-step kt (the tail re-loads the last one) into its stage
+    // this wavefront's share of the loads of K-step kt (the tail re-loads
+    // the last one), into its ring stage
     auto issue_stage = [&](int kt) __attribute__((always_inline)) {
       int kc = (kt < nk ? kt : nk - 1) + lag;
       if (kc >= nk) kc -= nk;
@@ -267,97 +291,65 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    // this wavefront's blocks (wm + i * WM) holding rows: a prefix i < nact
+    // this wavefront's blocks (grp + 2 i) holding rows: a prefix i < nact
     const int mblocks = (rows_valid + 31) / 32;
-    const int nact = min(FM, max(0, (mblocks - wm + WM - 1) / WM));
+    const int nact = min(FM, max(0, (mblocks - grp + WM - 1) / WM));
 
-    // the K loop for a wavefront with NACT active 32-row blocks (branch free)
-    //
-    // Software pipeline: the barrier of K-step kt sits before its last
-    // sub-step, so that the first fragments of K-step kt+1 are read while
-    // that sub-step's MFMAs run, and the loads for K-step kt+STAGES are
-    // issued right after it into the stage K-step kt has just finished
-    // reading.  Every K-step issues one stage of loads (the tail re-loads
-    // the last slice), so "stage kt+1 landed" is always vmcnt((STAGES-2) x
-    // loads per stage).
+    // Ping-pong over K-steps, for a wavefront with NACT active row blocks.
+    // Phase 2k:   group 0 reads K-step k (memory), group 1 multiplies k-1.
+    // Phase 2k+1: group 0 multiplies k, group 1 reads k.
+    // Stage k must be complete everywhere before phase 2k: every wavefront
+    // waits for its own share of it before the barrier that ends phase
+    // 2k-1 (group 0 after multiplying k-1, group 1 after reading k-1).
     auto k_loop = [&](auto nact_c) __attribute__((always_inline)) {
       constexpr int NACT = decltype(nact_c)::value;
       constexpr int NF = NACT > 0 ? NACT : 1;
-      constexpr int LPS = LA + LB;
-      static_assert(KSUB % 2 == 0, "fragment buffers alternate across K-steps");
-      bf16x8 fa[2][NF], fb[2][FN];
-      auto read_frags = [&](int stage, int kk, int buf) __attribute__((always_inline)) {
-        const char *sA = smem + stage * STAGE_BYTES;
-        const char *sB = sA + A_BYTES;
-        const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < NACT; ++i) {
-          const int row = (wm + i * WM) * 32 + (lane & 31);
-          fa[buf][i] = *(const bf16x8 *)(sA + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn * TN + j * 32 + (lane & 31);
-          fb[buf][j] = *(const bf16x8 *)(sB + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
-        }
-      };
-      auto mfmas = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NACT; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
-                                                                0, 0, 0);
-      };
-      constexpr int NMF = NACT * FN;  // MFMAs per sub-step
-      constexpr int NRD = NACT + FN;  // fragment reads per sub-step
-      // prologue: K-steps 0 .. STAGES-1 in flight, K-step 0's first fragments read
+      bf16x8 fa[KSUB][NF], fb[KSUB][FN];
+      // prologue: K-steps 0 .. STAGES-2 in flight, stage 0 complete
 #pragma unroll
       for (int p = 0; p < STAGES - 1; ++p) issue_stage(p);
       wait_vmcnt<(STAGES - 2) * LPS>();
       stage_barrier();
-      issue_stage(STAGES - 1);
-      if (NACT > 0) read_frags(0, 0, 0);
+      if (grp == 1) stage_barrier();  // group 1 runs one phase behind
       for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt % STAGES;
-#pragma unroll
-        for (int s = 0; s + 1 < KSUB; ++s) {
-          if (NACT > 0) read_frags(cur, s + 1, (s + 1) & 1);
-          mfmas(s & 1);
-        }
+        // memory phase: a later stage's loads, this K-step's fragments
+        issue_stage(kt + STAGES - 1);
         if (NACT > 0) {
-          // reads of the next sub-step between this sub-step's MFMAs
+          const char *sA = smem + (kt % STAGES) * STAGE_BYTES;
+          const char *sB = sA + A_BYTES;
 #pragma unroll
-          for (int s = 0; s + 1 < KSUB; ++s)
+          for (int s = 0; s < KSUB; ++s) {
+            const int c = s * 2 + (lane >> 5);
 #pragma unroll
-            for (int q = 0; q < NMF; ++q) {
-              __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-              if (q < NRD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            for (int i = 0; i < NACT; ++i) {
+              const int row = (grp + i * WM) * 32 + (lane & 31);
+              fa[s][i] = *(const bf16x8 *)(sA + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
             }
-        }
-        // K-step kt+1 has landed (this wavefront's part) and this
-        // wavefront's reads of K-step kt are done; after the barrier every
-        // part is visible and stage `cur` is free for K-step kt+STAGES
-        wait_vmcnt<(STAGES - 2) * LPS>();
-        wait_lgkmcnt0();
-        stage_barrier();
-        issue_stage(kt + STAGES);
-        if (NACT > 0) read_frags((kt + 1) % STAGES, 0, 0);
-        mfmas((KSUB - 1) & 1);
-        if (NACT > 0) {
-          // the next K-step's first reads, then this stage's loads, between
-          // the last sub-step's MFMAs
 #pragma unroll
-          for (int q = 0; q < NMF; ++q) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            if (q < NRD) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            else if (q < NRD + LPS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            for (int j = 0; j < FN; ++j) {
+              const int row = wn * TN + j * 32 + (lane & 31);
+              fb[s][j] = *(const bf16x8 *)(sB + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
+            }
           }
         }
+        wait_lgkmcnt0();
+        if (grp == 1) wait_vmcnt<(STAGES - 2) * LPS>();  // own share of stage kt+1
+        stage_barrier();
+        // compute phase
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s)
+#pragma unroll
+          for (int i = 0; i < NACT; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0,
+                                                                  0, 0);
+        if (grp == 0) wait_vmcnt<(STAGES - 2) * LPS>();  // own share of stage kt+1
+        stage_barrier();
       }
-      wait_vmcnt<0>();  // the tail's re-loads land before the stages are reused
+      if (grp == 0) stage_barrier();  // both groups pass the same number of barriers
+      wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
     };
-    static_assert(FM == 4, "k_loop dispatch below is written for four blocks per wavefront");
     switch (nact) {
       case 4: k_loop(std::integral_constant<int, 4>{}); break;
       case 3: k_loop(std::integral_constant<int, 3>{}); break;
@@ -374,18 +366,15 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i >= nact) continue;
-      const int rb = (wm + i * WM) * 32;
+      const int rb = (grp + i * WM) * 32;
       if (SWIGLU) {
+        const int col = n_tile * (BN / 2) + wn * (TN / 2) + (lane & 31);
 #pragma unroll
-        for (int p = 0; p < FN / 2; ++p) {
-          const int col = n_tile * (BN / 2) + wn * (TN / 2) + p * 32 + (lane & 31);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-            if (row < rows_valid) {
-              const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
-              C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(h);
-            }
+        for (int v = 0; v < 16; ++v) {
+          const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+          if (row < rows_valid) {
+            const float h = silu(acc[i][0][v]) * acc[i][1][v];
+            C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(h);
           }
         }
       } else {
@@ -409,14 +398,14 @@ __global__ __launch_bounds__(WM *WN *kWave) void grouped_gemm_kernel(MoeArgs a, 
   }
 }
 
-constexpr int kBM = 256, kBN = 256, kBK = 32, kWM = 2, kWN = 2, kStages = 4;
+constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 4;
 constexpr size_t kGemmLds = kStages * (size_t)(kBM + kBN) * kBK * 2;
 
 template <bool SWIGLU>
 hipError_t launch_gemm(const MoeArgs &a, const GemmDesc &g, int num_cus, hipStream_t st) {
   int nwg = ((num_cus + kNumXcd - 1) / kNumXcd) * kNumXcd;  // one workgroup per CU
-  auto kern = grouped_gemm_kernel<kBM, kBN, kBK, kWM, kWN, kStages, SWIGLU>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kWM * kWN * kWave), kGemmLds, st, a, g);
+  auto kern = grouped_gemm_kernel<kBM, kBN, kBK, kStages, SWIGLU>;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(8 * kWave), kGemmLds, st, a, g);
   return hipGetLastError();
 }
 
