@@ -62,11 +62,10 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
     }
   }
   u32x4 *orow = out + (int64_t)t * nvec;
-  for (int v = lane; v < nvec; v += kWave) {
-    u32x4 r[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < nk && src[j] != nullptr) r[j] = src[j][v];
+  // for K <= 8 two vectors per lane are in flight (2K row loads issued
+  // before any math); the rows are read once, so the loads stream past the
+  // caches
+  auto accumulate = [&](const u32x4 (&r)[KM]) __attribute__((always_inline)) {
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
@@ -86,7 +85,27 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
     o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
     o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
     o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-    orow[v] = o;
+    return o;
+  };
+  int v = lane;
+  if (KM <= 8)
+  for (; v + kWave < nvec; v += 2 * kWave) {
+    u32x4 r0[KM], r1[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < nk && src[j] != nullptr) {
+        r0[j] = __builtin_nontemporal_load(&src[j][v]);
+        r1[j] = __builtin_nontemporal_load(&src[j][v + kWave]);
+      }
+    orow[v] = accumulate(r0);
+    orow[v + kWave] = accumulate(r1);
+  }
+  for (; v < nvec; v += kWave) {
+    u32x4 r0[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < nk && src[j] != nullptr) r0[j] = __builtin_nontemporal_load(&src[j][v]);
+    orow[v] = accumulate(r0);
   }
 }
 
