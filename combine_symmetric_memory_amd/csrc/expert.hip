@@ -131,8 +131,8 @@ constexpr int kSchedDsRead = 0x100;
 // Both operands go global -> LDS through a STAGES-deep ring of direct
 // 16-byte-per-lane loads (XOR-swizzled rows, free of bank conflicts).  Time
 // is cut into phases by workgroup barriers; in every phase one group runs
-// only MFMAs on fragments already in registers while the other issues its
-// share of a later stage's loads and reads its next fragments from LDS.
+// only MFMAs on fragments already in registers while the other reads its
+// next fragments from LDS and then issues its share of a later stage's loads.
 // Group 1 starts one barrier late, so the two wavefronts of a SIMD always
 // sit in opposite phases and the matrix core never waits for memory.
 template <int BM, int BN, int BK, int STAGES, bool SWIGLU>
@@ -312,8 +312,10 @@ __global__ __launch_bounds__(8 * kWave) void grouped_gemm_kernel(MoeArgs a, Gemm
       stage_barrier();
       if (grp == 1) stage_barrier();  // group 1 runs one phase behind
       for (int kt = 0; kt < nk; ++kt) {
-        // memory phase: a later stage's loads, this K-step's fragments
-        issue_stage(kt + STAGES - 1);
+        // memory phase: this K-step's fragments, then a later stage's loads.
+        // The fragment reads go first: a wavefront issues in order, and its
+        // direct-to-LDS loads can sit in the issue queue until the address
+        // unit takes them; the LDS reads must not wait behind them.
         if (NACT > 0) {
           const char *sA = smem + (kt % STAGES) * STAGE_BYTES;
           const char *sB = sA + A_BYTES;
@@ -332,6 +334,7 @@ __global__ __launch_bounds__(8 * kWave) void grouped_gemm_kernel(MoeArgs a, Gemm
             }
           }
         }
+        issue_stage(kt + STAGES - 1);
         wait_lgkmcnt0();
         if (grp == 1) wait_vmcnt<(STAGES - 2) * LPS>();  // own share of stage kt+1
         stage_barrier();
