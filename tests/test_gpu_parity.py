@@ -97,13 +97,36 @@ def test_tiny_all_stages(ccm, orc):
 
 
 def test_multi_tile_ragged_experts(ccm, orc):
-    # ~256 rows per expert: several 128-row m-tiles per expert, ragged tails
+    # ~256 rows per expert: one or two 256-row m-tiles per expert, ragged tails
     cfg = get_config("tiny").with_(name="multitile", T=512, E=4, S=2, K=2, I=512, H=256)
     say("case: multi-tile", cfg)
     c = make_case(cfg)
     heap, moe = make_moe(cfg)
     out, code = run_path(moe, c)
     assert code == ccm.CCO_OK
+    _check_all_stages(orc, moe, c, out)
+    heap.destroy()
+
+
+def test_mixed_tile_shapes(ccm, orc):
+    # Expert row counts chosen around the 256-row m-tile: none, a small and a
+    # large remainder, exact multiples, 128 and 129 (the two remainder kinds
+    # meet there); H = 512 gives both GEMMs an even number of column tiles,
+    # so remainders of at most 128 rows take the 128-row, double-width tiles
+    counts = [306, 456, 100, 0, 512, 257, 128, 129]
+    cfg = get_config("tiny").with_(name="mixedtiles", E=8, S=4, K=2, H=512, I=512,
+                                   T=sum(counts) // 2)
+    say("case: mixed tile shapes", cfg, counts)
+    rng = np.random.default_rng(11)
+    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), counts)
+    rng.shuffle(flat)
+    idx = flat.reshape(cfg.T, cfg.K)
+    w = rng.random((cfg.T, cfg.K)).astype(np.float32)
+    c = make_case(cfg, idx_w=(idx, w))
+    heap, moe = make_moe(cfg)
+    out, code = run_path(moe, c)
+    assert code == ccm.CCO_OK
+    np.testing.assert_array_equal(moe.read_routing()[1], counts)
     _check_all_stages(orc, moe, c, out)
     heap.destroy()
 
