@@ -52,6 +52,7 @@ struct GemmDesc {
   int32_t lda;
   const uint16_t *w;     // B: weights of expert 0; expert e at w + e * w_estride
   int64_t w_estride;
+  int64_t w_bytes;       // bytes of one expert's weight matrix
   int32_t ldb;
   uint64_t c_win;        // C rows: window of the expert's slot, row stride ldc
   int32_t ldc;
@@ -75,12 +76,19 @@ __device__ __forceinline__ int rows_of(const MoeArgs &a, int e) {
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8), issued through the builtin so that the
 // compiler's own wait insertion sees them.
+// Both are scheduling barriers too: no instruction moves across a wait.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+  __builtin_amdgcn_sched_barrier(0);
 }
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
 // waits for every outstanding load, prefetches of later stages included.
@@ -92,12 +100,40 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
 
-// One 16-byte-per-lane direct load from global memory into LDS: lane l's
-// 16 bytes land at lds_base + 16 * l (lds_base is wavefront-uniform).
-__device__ __forceinline__ void load_lds_16(const void *gptr, char *lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t *)gptr, (lds_void_t *)lds_base, 16, 0, 0);
+// A wavefront-uniform value the compiler cannot prove uniform (it came from
+// memory) moved into scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char *uniform(const char *p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// LDS byte address (as the ds_* instructions see it) of a shared pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_char_t *)p;
+}
+
+// Buffer resource of a raw byte range (stride 0, 32-bit dword format word
+// of the gfx9 family); loads past num_bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range_rsrc(const void *base,
+                                                                  uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+
+// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes, read at
+// byte voff (per lane) + soff (wavefront-uniform) of the range, land at
+// lds_base + 16 * l (lds_base wavefront-uniform).  Only scalar work besides
+// the load itself: the offsets are registers the caller keeps.
+__device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   uint32_t soff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, (int)soff,
+                                           0, 0);
 }
 
 // LDS tile layout: rows of BK bf16 (ROWB bytes), unpadded, 16-byte chunks
@@ -128,19 +164,30 @@ constexpr int kSchedDsRead = 0x100;
 // (a 40 KiB stage) keeps the ring within the LDS with 3 stages.
 constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 4, kStagesHalf = 3;
 
-// Tile: BM rows x BN columns of one expert on 8 wavefronts, two per SIMD,
-// in a ping-pong schedule.  Wavefront (g, s) -- group g = wave / 4, SIMD
-// s = wave % 4 -- owns the 32-row blocks g, g+2, g+4, ... (interleaved, so a
-// half-empty tile still splits evenly) and columns [s*BN/4, (s+1)*BN/4), as
-// 32x32 blocks of v_mfma_f32_32x32x16_bf16.
+// Wavefronts per workgroup: one per SIMD.
+constexpr int kGemmWaves = 4;
+
+// Tile: BM rows x BN columns of one expert on 4 wavefronts, one per SIMD,
+// each owning a 128 x 128 block of the output as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 with the accumulators in AGPRs.  Wavefront w sits
+// at (wm, wn) = (w / WN, w % WN) of a WM x WN grid; its row blocks are
+// wm, wm + WM, wm + 2 WM, ... (interleaved, so a partly empty tile still
+// splits evenly) and its columns [wn * 128, wn * 128 + 128).
+//
+// The LDS operand reads set the pace: a SIMD moves about 26 bytes per clock
+// from LDS into registers, and a 4 x 4 block tile needs 8 fragment reads per
+// 16 MFMAs (1 KiB each) -- half an MFMA's worth of time per read, which the
+// MFMAs hide.  (Two wavefronts per SIMD halve the register budget; 4 x 2
+// block tiles then need 12 reads per 16 MFMAs, more than the matrix core's
+// time covers.)
 //
 // Both operands go global -> LDS through a STAGES-deep ring of direct
-// 16-byte-per-lane loads (XOR-swizzled rows, free of bank conflicts).  Time
-// is cut into phases by workgroup barriers; in every phase one group runs
-// only MFMAs on fragments already in registers while the other reads its
-// next fragments from LDS and then issues its share of a later stage's loads.
-// Group 1 starts one barrier late, so the two wavefronts of a SIMD always
-// sit in opposite phases and the matrix core never waits for memory.
+// 16-byte-per-lane buffer loads (XOR-swizzled rows, free of bank conflicts).
+// A K-step of 32 is two MFMA sub-steps; while one sub-step's MFMAs run, the
+// wavefront reads the next sub-step's fragments and issues its share of a
+// later stage's loads between them.  One barrier per K-step, between its
+// two sub-steps, makes the next stage visible to every wavefront and frees
+// the ring slot of the previous one.
 //
 // n_tile counts BN-wide column tiles (for gate/up: BN/2 intermediate
 // columns, gate and up interleaved in 32-row blocks); rows [row0, row0 +
@@ -150,8 +197,9 @@ template <int BM, int BN, int STAGES, bool SWIGLU>
 __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
                                          int n_tile, int row0, int rows_valid, int lag) {
   constexpr int BK = kBK;
-  constexpr int NW = 8;
-  constexpr int WM = 2, WN = 4;
+  constexpr int NW = kGemmWaves;
+  constexpr int WM = BM / 128;          // wavefront rows
+  constexpr int WN = NW / WM;           // wavefront columns
   constexpr int TN = BN / WN;           // columns per wavefront
   constexpr int FN = TN / 32;           // 32-column blocks per wavefront
   constexpr int MB = BM / 32;           // 32-row blocks per tile
@@ -165,23 +213,34 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   constexpr int LB = BN / (RPI * NW);   // B loads per wavefront per stage
   constexpr int LPS = LA + LB;
   constexpr int KSUB = BK / 16;         // MFMA sub-steps per K-step
+  static_assert(WM * WN == NW && FM == 4 && FN == 4, "4 x 4 blocks of 32 x 32 per wavefront");
+  static_assert(KSUB == 2, "a K-step is two MFMA sub-steps");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
-  static_assert(!SWIGLU || FN % 2 == 0, "gate/up: gate and up blocks come in pairs");
   static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
   static_assert(STAGES >= 3 && (STAGES - 2) * LPS < 64, "stage count / vmcnt range");
-  static_assert(FM >= 1 && FN >= 1, "tile too small for 8 wavefronts");
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int grp = wave / WN;   // ping-pong group == row half
-  const int wn = wave % WN;    // SIMD == column quarter
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  // the tile's parameters are wavefront-uniform; keep them (and the operand
+  // descriptors built from them) in scalar registers
+  e = uniform(e);
+  n_tile = uniform(n_tile);
+  row0 = uniform(row0);
+  rows_valid = uniform(rows_valid);
+  lag = uniform(lag);
   const int slot = e / a.eps;
-  const int64_t grow0 = (int64_t)a.expert_off[e] + row0;
+  const int64_t grow0 = (int64_t)uniform(a.expert_off[e]) + row0;
   const int nk = g.kdim / BK;
 
-  const char *A = slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2);
-  const char *B = (const char *)(g.w + (int64_t)e * g.w_estride);
+  const char *A = uniform(slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2));
+  const char *B = uniform((const char *)(g.w + (int64_t)e * g.w_estride));
+  // operand byte ranges: the tile's receive rows, the expert's weights
+  const __amdgpu_buffer_rsrc_t ra =
+      byte_range_rsrc(A, (uint32_t)rows_valid * (uint32_t)g.lda * 2u);
+  const __amdgpu_buffer_rsrc_t rb = byte_range_rsrc(B, (uint32_t)g.w_bytes);
 
   // byte offset (at k = 0) of the chunk each lane loads; rows past the
   // expert's last row re-read that row, so the load count never varies
@@ -193,6 +252,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     const int row = (q * NW + wave) * RPI + ld_row;
     const int rr = row < rows_valid ? row : rows_valid - 1;
     oa[q] = (uint32_t)rr * (uint32_t)g.lda * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
+    asm volatile("" : "+v"(oa[q]));
   }
 #pragma unroll
   for (int q = 0; q < LB; ++q) {
@@ -207,130 +267,221 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       grow = (uint32_t)(n_tile * BN + row);
     }
     ob[q] = grow * (uint32_t)g.ldb * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
+    asm volatile("" : "+v"(ob[q]));
   }
-  // this wavefront's share of the loads of K-step kt (the tail re-loads the
-  // last one), into its ring stage; K-steps run from lag, wrapping
-  auto issue_stage = [&](int kt) __attribute__((always_inline)) {
+  // LDS fragment addresses, per ring stage and MFMA sub-step.  The rows of
+  // one wavefront's blocks differ by multiples of 32, so they share the row
+  // swizzle and differ by constant offsets (folded into the instructions).
+  // Kept opaque so the compiler does not recompute them inside the loop.
+  uint32_t fa_addr[STAGES][KSUB], fb_addr[STAGES][KSUB];
+  {
+    const int l = lane & 31;
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st)
+#pragma unroll
+      for (int sk = 0; sk < KSUB; ++sk) {
+        const int c = sk * 2 + (lane >> 5);
+        const uint32_t lp = (uint32_t)(l * ROWB + ((c ^ swz<CPR>(l)) * 16));
+        fa_addr[st][sk] = base + st * STAGE_BYTES + wm * 32 * ROWB + lp;
+        fb_addr[st][sk] = base + st * STAGE_BYTES + A_BYTES + wn * TN * ROWB + lp;
+        asm volatile("" : "+v"(fa_addr[st][sk]), "+v"(fb_addr[st][sk]));
+      }
+  }
+
+  // load q (0 .. LPS-1: A loads, then B loads) of this wavefront's share of
+  // K-step kt (the tail re-loads the last one) into ring stage ST; K-steps
+  // run from lag, wrapping.  Scalar offsets only.
+  auto issue_load = [&](auto st_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value, q = decltype(q_c)::value;
+    char *sbase = smem + ST * STAGE_BYTES;
+    if constexpr (q < LA)
+      buffer_load_lds_16(ra, oa[q], soff, sbase + (q * NW + wave) * 1024);
+    else
+      buffer_load_lds_16(rb, ob[q - LA], soff, sbase + A_BYTES + ((q - LA) * NW + wave) * 1024);
+  };
+  auto k_offset = [&](int kt) __attribute__((always_inline)) {
     int kc = (kt < nk ? kt : nk - 1) + lag;
     if (kc >= nk) kc -= nk;
-    char *sbase = smem + (kt % STAGES) * STAGE_BYTES;
-    const char *Ak = A + (int64_t)kc * ROWB;
-    const char *Bk = B + (int64_t)kc * ROWB;
-#pragma unroll
-    for (int q = 0; q < LA; ++q) load_lds_16(Ak + oa[q], sbase + (q * NW + wave) * 1024);
-#pragma unroll
-    for (int q = 0; q < LB; ++q)
-      load_lds_16(Bk + ob[q], sbase + A_BYTES + (q * NW + wave) * 1024);
+    return (uint32_t)kc * ROWB;
   };
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  // this wavefront's blocks (grp + 2 i) holding rows: a prefix i < nact
+  // this wavefront's blocks (wm + WM i) holding rows: a prefix i < nact
   const int mblocks = (rows_valid + 31) / 32;
-  const int nact = min(FM, max(0, (mblocks - grp + WM - 1) / WM));
+  const int nact = min(FM, max(0, (mblocks - wm + WM - 1) / WM));
+  uint16_t *C = (uint16_t *)slot_addr(a, slot, g.c_win, (uint64_t)grow0 * g.ldc * 2);
 
-  // Ping-pong over K-steps, for a wavefront with NACT active row blocks.
-  // Phase 2k:   group 0 reads K-step k (memory), group 1 multiplies k-1.
-  // Phase 2k+1: group 0 multiplies k, group 1 reads k.
-  // Stage k must be complete everywhere before phase 2k: every wavefront
-  // waits for its own share of it before the barrier that ends phase 2k-1
-  // (group 0 after multiplying k-1, group 1 after reading k-1).
+  // The whole tile for a wavefront with NACT active row blocks: the
+  // accumulators live only inside one specialisation.
   auto k_loop = [&](auto nact_c) __attribute__((always_inline)) {
     constexpr int NACT = decltype(nact_c)::value;
     constexpr int NF = NACT > 0 ? NACT : 1;
-    bf16x8 fa[KSUB][NF], fb[KSUB][FN];
-    // prologue: K-steps 0 .. STAGES-2 in flight, stage 0 complete
+    f32x16 acc[NF][FN];
 #pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p) issue_stage(p);
+    for (int i = 0; i < NF; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    constexpr int NRD = NACT > 0 ? NACT + FN : 0;  // fragment reads per sub-step
+    constexpr int H0 = LPS / 2;                     // loads issued in sub-step 0
+    constexpr int H1 = LPS - H0;                    // ... and in sub-step 1
+    // fragments of the two sub-steps (double buffer: one is multiplied while
+    // the other is read).  Read order: the FN B fragments, then the NACT A
+    // fragments, so that row i of MFMAs can start once A fragment i is in.
+    bf16x8 fa[2][NF], fb[2][FN];
+    auto read_frag = [&](auto buf_c, auto st_c, auto sk_c, auto r_c) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(buf_c)::value, ST = decltype(st_c)::value;
+      constexpr int SK = decltype(sk_c)::value, r = decltype(r_c)::value;
+      if constexpr (r < FN)
+        fb[BUF][r] = *((lds_bf16x8_t *)(uintptr_t)fb_addr[ST][SK] + r * 32 * ROWB / 16);
+      else
+        fa[BUF][r - FN] =
+            *((lds_bf16x8_t *)(uintptr_t)fa_addr[ST][SK] + (r - FN) * WM * 32 * ROWB / 16);
+    };
+    // lgkmcnt wait (in-order LDS returns): at most N reads outstanding
+    auto wait_lgkm = [&](auto n_c) __attribute__((always_inline)) {
+      constexpr int N = decltype(n_c)::value;
+      static_assert(N >= 0 && N < 16, "lgkmcnt range");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8) | (N << 8));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // prologue: K-steps 0 .. STAGES-2 in flight; stage 0 complete
+    // everywhere; the fragments of (K-step 0, sub-step 0) read into buffer 0
+    static_for<STAGES - 1>([&](auto p_c) __attribute__((always_inline)) {
+      const uint32_t soff = k_offset(decltype(p_c)::value);
+      static_for<LPS>([&](auto q_c) __attribute__((always_inline)) { issue_load(p_c, q_c, soff); });
+    });
     wait_vmcnt<(STAGES - 2) * LPS>();
     stage_barrier();
-    if (grp == 1) stage_barrier();  // group 1 runs one phase behind
-    for (int kt = 0; kt < nk; ++kt) {
-      // memory phase: this K-step's fragments, then a later stage's loads.
-      // The fragment reads go first: a wavefront issues in order, and its
-      // direct-to-LDS loads can sit in the issue queue until the address
-      // unit takes them; the LDS reads must not wait behind them.
-      if (NACT > 0) {
-        const char *sA = smem + (kt % STAGES) * STAGE_BYTES;
-        const char *sB = sA + A_BYTES;
-#pragma unroll
-        for (int s = 0; s < KSUB; ++s) {
-          const int c = s * 2 + (lane >> 5);
-#pragma unroll
-          for (int i = 0; i < NACT; ++i) {
-            const int row = (grp + i * WM) * 32 + (lane & 31);
-            fa[s][i] = *(const bf16x8 *)(sA + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
+    static_for<NRD>([&](auto r_c) __attribute__((always_inline)) { read_frag(I0{}, I0{}, I0{}, r_c); });
+
+    // K-step kt, whose stage is ST = kt % STAGES.  Each wavefront issues, in
+    // order (one item after each MFMA):
+    //  sub-step 0: MFMAs of (kt, 0) from buffer 0; items: the reads of
+    //    (kt, 1) into buffer 1, then H0 loads of K-step kt+STAGES-1 (into
+    //    the slot K-step kt-1 used, free since the previous barrier);
+    //  sub-step 1: MFMAs of (kt, 1) from buffer 1; after the first row:
+    //    wait for its own share of stage kt+1, barrier (stage kt+1 complete
+    //    everywhere); items: the reads of (kt+1, 0) into buffer 0, then the
+    //    other H1 loads.
+    // Before MFMA row i, a progressive lgkmcnt wait lets the row start as
+    // soon as its A fragment (and the B fragments read before it) are in.
+    auto step = [&](auto st_c, int kt) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr int NST = (ST + 1) % STAGES;            // stage of K-step kt+1
+      constexpr int LST = (ST + STAGES - 1) % STAGES;   // stage of K-step kt+STAGES-1
+      const uint32_t soff = k_offset(kt + STAGES - 1);
+      // ---- sub-step 0
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        // new reads issued before row i: one per earlier MFMA, at most NRD
+        constexpr int ISSUED = (i * FN < NRD) ? i * FN : NRD;
+        wait_lgkm(std::integral_constant<int, (NACT - 1 - i) + ISSUED>{});
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value, m = i * FN + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], acc[i][j], 0, 0, 0);
+          if constexpr (m < NRD) read_frag(I1{}, st_c, I1{}, std::integral_constant<int, m>{});
+          else if constexpr (m - NRD < H0)
+            issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, m - NRD>{}, soff);
+        });
+      });
+      // items the MFMAs did not cover (few active rows)
+      constexpr int NMF = NACT * FN;
+      static_for<(NRD + H0 > NMF) ? NRD + H0 - NMF : 0>([&](auto t_c) __attribute__((always_inline)) {
+        constexpr int m = NMF + decltype(t_c)::value;
+        if constexpr (m < NRD) read_frag(I1{}, st_c, I1{}, std::integral_constant<int, m>{});
+        else issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, m - NRD>{}, soff);
+      });
+      // ---- sub-step 1
+      auto sync = [&]() __attribute__((always_inline)) {
+        wait_vmcnt<(STAGES - 3) * LPS + H0>();  // own share of stage kt+1
+        stage_barrier();                        // stage kt+1 complete everywhere
+      };
+      if constexpr (NACT == 0) sync();
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        // items start after row 0 (and the barrier)
+        constexpr int ISSUED = (i == 0) ? 0 : (((i - 1) * FN < NRD) ? (i - 1) * FN : NRD);
+        wait_lgkm(std::integral_constant<int, (NACT - 1 - i) + ISSUED>{});
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value, m = (i - 1) * FN + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+          if constexpr (i >= 1) {
+            if constexpr (m < NRD) read_frag(I0{}, std::integral_constant<int, NST>{}, I0{}, std::integral_constant<int, m>{});
+            else if constexpr (m - NRD < H1)
+              issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, H0 + m - NRD>{}, soff);
           }
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int row = wn * TN + j * 32 + (lane & 31);
-            fb[s][j] = *(const bf16x8 *)(sB + row * ROWB + ((c ^ swz<CPR>(row)) * 16));
-          }
-        }
-      }
-      issue_stage(kt + STAGES - 1);
-      wait_lgkmcnt0();
-      if (grp == 1) wait_vmcnt<(STAGES - 2) * LPS>();  // own share of stage kt+1
-      stage_barrier();
-      // compute phase
-#pragma unroll
-      for (int s = 0; s < KSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < NACT; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-      if (grp == 0) wait_vmcnt<(STAGES - 2) * LPS>();  // own share of stage kt+1
-      stage_barrier();
-    }
-    if (grp == 0) stage_barrier();  // both groups pass the same number of barriers
+        });
+        if constexpr (i == 0) sync();
+      });
+      constexpr int NMF1 = NACT > 0 ? (NACT - 1) * FN : 0;
+      static_for<(NRD + H1 > NMF1) ? NRD + H1 - NMF1 : 0>([&](auto t_c) __attribute__((always_inline)) {
+        constexpr int m = NMF1 + decltype(t_c)::value;
+        if constexpr (m < NRD) read_frag(I0{}, std::integral_constant<int, NST>{}, I0{}, std::integral_constant<int, m>{});
+        else issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, H0 + m - NRD>{}, soff);
+      });
+    };
+    // K-steps in rounds of STAGES, so that each step's stage is a constant
+    int kt = 0;
+    for (; kt + STAGES <= nk; kt += STAGES)
+      static_for<STAGES>([&](auto p) __attribute__((always_inline)) {
+        step(p, kt + decltype(p)::value);
+      });
+    static_for<STAGES - 1>([&](auto p) __attribute__((always_inline)) {
+      if (kt + decltype(p)::value < nk) step(p, kt + decltype(p)::value);
+    });
+    wait_lgkm(I0{});
     wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
+    // every wavefront is done with the LDS before the next tile refills it
+    __syncthreads();
+
+    // epilogue: lane holds column (lane % 32) of each 32x32 block, rows
+    // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v.  One
+    // block (pair) at a time: the empty asm statements pin each block's
+    // reads after the previous block's stores, which keeps the compiler from
+    // hoisting every accumulator into VGPRs at once.
+    static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      const int rb = (wm + i * WM) * 32;
+      if constexpr (SWIGLU) {
+        static_for<FN / 2>([&](auto p_c) __attribute__((always_inline)) {
+          constexpr int p = decltype(p_c)::value;
+          asm volatile("" : "+a"(acc[i][2 * p]), "+a"(acc[i][2 * p + 1]));
+          const int col = n_tile * (BN / 2) + wn * (TN / 2) + p * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+            if (row < rows_valid) {
+              const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
+              C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(h);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          asm volatile("" : "+a"(acc[i][j]));
+          const int col = n_tile * BN + wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+            if (row < rows_valid) C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(acc[i][j][v]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+    });
   };
   // one specialisation per active-block count (wavefront-uniform branch)
   static_for<FM + 1>([&](auto c) __attribute__((always_inline)) {
     if (nact == decltype(c)::value) k_loop(c);
   });
-  // every wavefront is done with the LDS before the next tile refills it
-  __syncthreads();
-
-  // epilogue: lane holds column (lane % 32) of each 32x32 block, rows
-  // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v
-  uint16_t *C = (uint16_t *)slot_addr(a, slot, g.c_win, (uint64_t)grow0 * g.ldc * 2);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    if (i >= nact) continue;
-    const int rb = (grp + i * WM) * 32;
-    if (SWIGLU) {
-#pragma unroll
-      for (int p = 0; p < FN / 2; ++p) {
-        const int col = n_tile * (BN / 2) + wn * (TN / 2) + p * 32 + (lane & 31);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-          if (row < rows_valid) {
-            const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
-            C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(h);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n_tile * BN + wn * TN + j * 32 + (lane & 31);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-          if (row < rows_valid) C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(acc[i][j][v]);
-        }
-      }
-    }
-  }
 }
 
 // Work list of one expert: its rows R = 256 q + r are covered by q full
@@ -359,13 +510,21 @@ __device__ __forceinline__ ExpertTiles expert_tiles(int rows, int ntl) {
 // side by side; with a half remainder, the pair of column tiles (2j, 2j+1)
 // lists its full m-tiles and then the remainder tile j that spans both.
 template <bool SWIGLU>
-__global__ __launch_bounds__(8 * kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
-  constexpr int NT = 8 * kWave;
+__global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
+  constexpr int NT = kGemmWaves * kWave;
   extern __shared__ __align__(1024) char smem[];  // the ring of the running tile shape
   __shared__ int32_t tile_prefix[kMaxExperts + 1];
-  __shared__ int32_t scan_tmp[8];
+  __shared__ int32_t scan_tmp[kGemmWaves];
   __shared__ int32_t next_tile;
 
+  // Keep the MFMA accumulators in AGPRs.  With two wavefronts per SIMD the
+  // kernel fits in 256 registers, and the compiler then picks the form of
+  // v_mfma that reads and writes C/D in ordinary VGPRs; on gfx950 that form
+  // draws more power, and the clock drops (a register-only MFMA loop ran 1.83
+  // PFLOP/s with AGPR accumulators vs 1.32 with VGPR ones, random bf16
+  // operands).  An empty asm statement that clobbers an AGPR marks the
+  // kernel as using AGPRs, which selects the AGPR form.
+  asm volatile("" ::: "a0");
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -417,7 +576,9 @@ __global__ __launch_bounds__(8 * kWave) void grouped_gemm_kernel(MoeArgs a, Gemm
   for (;;) {
     if (tid == 0) next_tile = t_begin + atomicAdd(&g.queue[xcd], 1);
     __syncthreads();
-    const int L = next_tile;
+    // the tile index and everything derived from it are wavefront-uniform:
+    // keep them in scalar registers, so that per-K-step offsets stay scalar
+    const int L = __builtin_amdgcn_readfirstlane(next_tile);
     if (L >= t_end) break;
 
     // expert e owns list entries [prefix[e], prefix[e+1])
@@ -426,8 +587,8 @@ __global__ __launch_bounds__(8 * kWave) void grouped_gemm_kernel(MoeArgs a, Gemm
       const int mid = (lo + hi) >> 1;
       if (tile_prefix[mid] <= L) lo = mid; else hi = mid;
     }
-    const int e = lo;
-    const int rows = rows_of(a, e);
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int rows = __builtin_amdgcn_readfirstlane(rows_of(a, e));
     const ExpertTiles et = expert_tiles(rows, ntl);
     const int r = L - tile_prefix[e];
     // Tiles sharing a weight panel or receive rows run side by side on one
@@ -471,7 +632,7 @@ template <bool SWIGLU>
 hipError_t launch_gemm(const MoeArgs &a, const GemmDesc &g, int num_cus, hipStream_t st) {
   int nwg = ((num_cus + kNumXcd - 1) / kNumXcd) * kNumXcd;  // one workgroup per CU
   auto kern = grouped_gemm_kernel<SWIGLU>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(8 * kWave), kGemmLds, st, a, g);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kGemmWaves * kWave), kGemmLds, st, a, g);
   return hipGetLastError();
 }
 
@@ -484,6 +645,7 @@ hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int num_
   g.lda = a.H;
   g.w = w13;
   g.w_estride = (int64_t)2 * a.I * a.H;
+  g.w_bytes = g.w_estride * 2;
   g.ldb = a.H;
   g.c_win = a.off_hbuf;
   g.ldc = a.I;
@@ -501,6 +663,7 @@ hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int num_cus,
   g.lda = a.I;
   g.w = w2;
   g.w_estride = (int64_t)a.H * a.I;
+  g.w_bytes = g.w_estride * 2;
   g.ldb = a.I;
   g.c_win = a.off_out;
   g.ldc = a.H;
