@@ -160,9 +160,10 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 
-// Full tile 256 x 256 x 32 with a 4-deep ring; the 128 x 512 remainder tile
-// (a 40 KiB stage) keeps the ring within the LDS with 3 stages.
-constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 4, kStagesHalf = 3;
+// Full tile 256 x 256 x 32 with a 5-deep ring (32 KiB stages); the 128 x 512
+// remainder tile (40 KiB stages) with 4.  Either ring fills the 160 KiB of
+// LDS, so the kernel keeps nothing else there.
+constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 5, kStagesHalf = 4;
 
 // Wavefronts per workgroup: one per SIMD.
 constexpr int kGemmWaves = 4;
@@ -512,10 +513,11 @@ __device__ __forceinline__ ExpertTiles expert_tiles(int rows, int ntl) {
 template <bool SWIGLU>
 __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
   constexpr int NT = kGemmWaves * kWave;
-  extern __shared__ __align__(1024) char smem[];  // the ring of the running tile shape
-  __shared__ int32_t tile_prefix[kMaxExperts + 1];
-  __shared__ int32_t scan_tmp[kGemmWaves];
-  __shared__ int32_t next_tile;
+  // The ring of the running tile shape takes all of the LDS.  Between tiles
+  // (and before the first) it is idle, and its first words serve as scratch
+  // for the tile hand-out.
+  extern __shared__ __align__(1024) char smem[];
+  int32_t *scratch = (int32_t *)smem;
 
   // Keep the MFMA accumulators in AGPRs.  With two wavefronts per SIMD the
   // kernel fits in 256 registers, and the compiler then picks the form of
@@ -531,10 +533,12 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   const int E = a.E;
   const int ntl = g.ntiles;
 
-  // tiles per expert -> exclusive prefix over experts
+  // tiles per expert and their exclusive prefix over experts, held in
+  // registers: thread t owns experts t * PER .. t * PER + PER - 1
+  constexpr int PER = (kMaxExperts + NT - 1) / NT;
+  int32_t loc[PER], pre[PER];
+  int total;
   {
-    constexpr int PER = (kMaxExperts + NT - 1) / NT;
-    int32_t loc[PER];
     int32_t sum = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -548,21 +552,24 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
       const int32_t up = __shfl_up(incl, d, kWave);
       if (lane >= d) incl += up;
     }
-    if (lane == kWave - 1) scan_tmp[wave] = incl;
+    if (lane == kWave - 1) scratch[wave] = incl;
     __syncthreads();
     int32_t run = incl - sum;
-    for (int w = 0; w < wave; ++w) run += scan_tmp[w];
+    total = 0;
+    for (int w = 0; w < kGemmWaves; ++w) {
+      const int32_t wt = scratch[w];
+      if (w < wave) run += wt;
+      total += wt;
+    }
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int e = tid * PER + q;
-      if (e <= E) tile_prefix[e] = run;
+      pre[q] = run;
       run += loc[q];
     }
-    if (tid == NT - 1) tile_prefix[E] = run;  // the total (E may equal NT * PER)
+    total = uniform(total);
     __syncthreads();
   }
 
-  const int total = tile_prefix[E];
   // tiles are split into kNumXcd contiguous ranges; the workgroups of XCD x
   // (block id % kNumXcd, the hardware's round-robin placement) take the
   // tiles of range x in order from a counter, so the tiles running at once
@@ -574,23 +581,25 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   const int nk = g.kdim / kBK;
 
   for (;;) {
-    if (tid == 0) next_tile = t_begin + atomicAdd(&g.queue[xcd], 1);
+    if (tid == 0) scratch[0] = t_begin + atomicAdd(&g.queue[xcd], 1);
     __syncthreads();
     // the tile index and everything derived from it are wavefront-uniform:
     // keep them in scalar registers, so that per-K-step offsets stay scalar
-    const int L = __builtin_amdgcn_readfirstlane(next_tile);
+    const int L = uniform(scratch[0]);
     if (L >= t_end) break;
-
-    // expert e owns list entries [prefix[e], prefix[e+1])
-    int lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tile_prefix[mid] <= L) lo = mid; else hi = mid;
-    }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int rows = __builtin_amdgcn_readfirstlane(rows_of(a, e));
+    // the thread owning expert e with L in [pre, pre + loc) posts (e, L - pre)
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (L >= pre[q] && L < pre[q] + loc[q]) {
+        scratch[1] = tid * PER + q;
+        scratch[2] = L - pre[q];
+      }
+    __syncthreads();
+    const int e = uniform(scratch[1]);
+    const int r = uniform(scratch[2]);
+    __syncthreads();  // scratch read everywhere before the ring refills
+    const int rows = uniform(rows_of(a, e));
     const ExpertTiles et = expert_tiles(rows, ntl);
-    const int r = L - tile_prefix[e];
     // Tiles sharing a weight panel or receive rows run side by side on one
     // XCD; rotating the K order by a small tile-dependent lag keeps them from
     // missing the same L2 lines at the same moment.
