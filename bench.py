@@ -26,12 +26,18 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+# arithmetic intensity (flop per HBM byte) above which a kernel is bound by
+# the matrix cores rather than by HBM
+RIDGE_FLOP_PER_BYTE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+FLUSH_BYTES = 1 << 30       # written between timed iterations: evicts L2 and MALL
 
 
-def stage_work(cfg):
+def stage_work(cfg, active_experts=None):
     """Algorithmic bytes / flops per launch of each kernel (what the method
-    must move or compute; not what a kernel happens to re-read)."""
+    must move or compute; not what a kernel happens to re-read).  Expert
+    weights count once per expert that received rows."""
     T, H, K, E, I = cfg.T, cfg.H, cfg.K, cfg.E, cfg.I
+    EA = E if active_experts is None else int(active_experts)
     TK = T * K
     w = {
         # plan: read idx twice (count, rank), write pos + expert ids, counts/offsets
@@ -44,9 +50,9 @@ def stage_work(cfg):
     }
     if I > 0:
         # gate/up: X rows, gate+up weights of the active experts, h out
-        w["expert_gate_up"] = dict(flops=4 * TK * H * I, bytes=2 * TK * H + 4 * E * I * H + 2 * TK * I)
+        w["expert_gate_up"] = dict(flops=4 * TK * H * I, bytes=2 * TK * H + 4 * EA * I * H + 2 * TK * I)
         # down: h rows, down weights, y out
-        w["expert_down"] = dict(flops=2 * TK * H * I, bytes=2 * TK * I + 2 * E * H * I + 2 * TK * H)
+        w["expert_down"] = dict(flops=2 * TK * H * I, bytes=2 * TK * I + 2 * EA * H * I + 2 * TK * H)
     return w
 
 
@@ -189,21 +195,30 @@ def main():
     log("timed %d steps: %.3f ms/step (events %.3f ms/step)" % (args.steps, ms_per_step,
                                                                   gpu_ms / args.steps))
 
-    # ---- per-kernel durations: HIP events on the launch stream ----
+    # ---- per-kernel durations: HIP events on the launch stream, one step per
+    # iteration, L2 and MALL evicted before each (1 GiB written) ----
+    flush = torch.empty(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    n_iter = max(20, min(args.steps, 50))
+    per = {}
     moe.set_timing(True)
-    nt = max(3, min(args.steps, 10))
-    for _ in range(nt):
+    for _ in range(n_iter):
+        flush.fill_(1.0)
         step()
-    torch.cuda.synchronize()
-    summ = moe.timing_summary()
+        torch.cuda.synchronize()
+        for k, (n, ms) in moe.timing_summary().items():
+            if n:
+                per.setdefault(k, []).append(ms / n)
     moe.set_timing(False)
-    work = stage_work(cfg)
+    del flush
+    work = stage_work(cfg, active_experts=int(np.count_nonzero(counts)))
     stages = {}
-    for k, (n, ms) in summ.items():
-        if n == 0:
-            continue
-        avg = ms / n
-        st = {"launches": n, "avg_ms": round(avg, 5)}
+    for k, times in per.items():
+        t = np.asarray(times)
+        avg = float(t.mean())
+        st = {"launches": len(times), "avg_ms": round(avg, 5),
+              "median_ms": round(float(np.median(t)), 5),
+              "p10_ms": round(float(np.percentile(t, 10)), 5),
+              "p90_ms": round(float(np.percentile(t, 90)), 5)}
         wk = work.get(k, {})
         if "bytes" in wk:
             st["alg_bytes"] = wk["bytes"]
@@ -213,22 +228,27 @@ def main():
             st["alg_flops"] = wk["flops"]
             st["TFLOP_s"] = round(wk["flops"] / (avg * 1e-3) / 1e12, 2)
             st["mfma_frac"] = round(st["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)
+            st["flop_per_byte"] = round(wk["flops"] / wk["bytes"], 1)
         stages[k] = st
     log("stages", json.dumps(stages))
 
-    if cfg.I > 0:
-        dom = "expert_gate_up"
-        d = stages[dom]
-        roofline = {"kernel": dom, "bound": "mfma", "achieved": d["TFLOP_s"],
-                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["mfma_frac"],
-                    "traffic": profiled_traffic(cfg.name, dom),
-                    "hbm_view": {"alg_bytes": d["alg_bytes"], "GB_s": d["GB_s"],
-                                 "frac": d["hbm_frac"]}}
+    # roofline of the dominant kernel (the longest one), bound by HBM or by
+    # the matrix cores according to its arithmetic intensity
+    dom = max(stages, key=lambda k: stages[k]["avg_ms"])
+    d = stages[dom]
+    hbm = {"achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["hbm_frac"]}
+    if "alg_flops" in d:
+        mfma = {"achieved": d["TFLOP_s"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": d["mfma_frac"]}
+        if d["flop_per_byte"] < RIDGE_FLOP_PER_BYTE:
+            roofline = dict(kernel=dom, bound="hbm", **hbm, mfma_view=mfma)
+        else:
+            roofline = dict(kernel=dom, bound="mfma", **mfma, hbm_view=hbm)
+        roofline["flop_per_byte"] = d["flop_per_byte"]
+        roofline["ridge_flop_per_byte"] = round(RIDGE_FLOP_PER_BYTE, 1)
     else:
-        dom = max(("dispatch", "combine"), key=lambda k: stages[k]["avg_ms"])
-        d = stages[dom]
-        roofline = {"kernel": dom, "bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": d["hbm_frac"], "traffic": profiled_traffic(cfg.name, dom)}
+        roofline = dict(kernel=dom, bound="hbm", **hbm)
+    roofline["traffic"] = profiled_traffic(cfg.name, dom)
 
     dc_bytes = stages["dispatch"]["alg_bytes"] + stages["combine"]["alg_bytes"]
     dc_ms = stages["dispatch"]["avg_ms"] + stages["combine"]["avg_ms"]
