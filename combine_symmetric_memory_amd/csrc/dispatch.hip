@@ -9,8 +9,8 @@
 //
 // One wavefront per token.  The token's K destinations are wave-uniform
 // (scalar loads of idx and pos), the row is read once in 16-byte vectors
-// and each vector is stored K times; 64 lanes x 16 B make every store
-// instruction one contiguous 1 KiB run.  Lanes 0..K-1 also write the
+// (up to 16 per lane in flight) and each vector is stored K times; 64 lanes
+// x 16 B make every store instruction one contiguous 1 KiB run.  Lanes 0..K-1 also write the
 // per-row metadata {t*K + j, w[t][j], e}.
 #include "cco_internal.h"
 
@@ -46,25 +46,26 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
         dst[j] = (u32x4 *)slot_addr(a, e / a.eps, a.off_disp_x, (uint64_t)p * rb);
     }
   }
-  // four vectors in flight per lane, then the tail one at a time
-  int v = lane;
-  for (; v + 3 * kWave < nvec; v += 4 * kWave) {
-    const u32x4 r0 = xr[v], r1 = xr[v + kWave], r2 = xr[v + 2 * kWave], r3 = xr[v + 3 * kWave];
+  // the row in chunks of up to kChunk vectors per lane (the whole row for
+  // H <= 8192): all of a chunk's loads are in flight before its K stores
+  constexpr int kChunk = 16;
+  for (int v0 = 0; v0 < nvec; v0 += kChunk * kWave) {
+    u32x4 r[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int v = v0 + c * kWave + lane;
+      if (v < nvec) r[c] = xr[v];
+    }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j < nk && dst[j] != nullptr) {
-        dst[j][v] = r0;
-        dst[j][v + kWave] = r1;
-        dst[j][v + 2 * kWave] = r2;
-        dst[j][v + 3 * kWave] = r3;
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+          const int v = v0 + c * kWave + lane;
+          if (v < nvec) dst[j][v] = r[c];
+        }
       }
     }
-  }
-  for (; v < nvec; v += kWave) {
-    const u32x4 r0 = xr[v];
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < nk && dst[j] != nullptr) dst[j][v] = r0;
   }
   if (lane < nk) {
     const int f = t * nk + lane;
