@@ -131,6 +131,23 @@ def test_mixed_tile_shapes(ccm, orc):
     heap.destroy()
 
 
+@pytest.mark.parametrize("K,E,S,T", [
+    (3, 16, 4, 100),      # odd top-k: the kernels' generic-K path
+    (5, 16, 4, 77),
+    (32, 64, 8, 40),      # the largest top-k
+    (8, 1024, 8, 96),     # the largest expert count (most experts empty)
+])
+def test_generic_topk_and_limits(ccm, orc, K, E, S, T):
+    cfg = get_config("tiny").with_(name="limits", K=K, E=E, S=S, T=T, H=256, I=256)
+    say("case: K=%d E=%d S=%d T=%d" % (K, E, S, T))
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    out, code = run_path(moe, c)
+    assert code == ccm.CCO_OK
+    _check_all_stages(orc, moe, c, out)
+    heap.destroy()
+
+
 @pytest.mark.parametrize("T", [0, 1, 37, 127])
 def test_ragged_token_counts(ccm, orc, T):
     cfg = get_config("tiny")
