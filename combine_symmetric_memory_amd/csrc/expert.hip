@@ -39,13 +39,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32, which
+// the compiler emits for a plain conversion (two values per instruction).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z); the reciprocal is the hardware's (about 1 ulp of
+// fp32), far below the bf16 rounding that follows.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 struct GemmDesc {
   uint64_t a_win;        // A rows: window of the expert's slot, row stride lda
@@ -441,43 +445,59 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     // every wavefront is done with the LDS before the next tile refills it
     __syncthreads();
 
-    // epilogue: lane holds column (lane % 32) of each 32x32 block, rows
-    // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v.  One
-    // block (pair) at a time: the empty asm statements pin each block's
-    // reads after the previous block's stores, which keeps the compiler from
-    // hoisting every accumulator into VGPRs at once.
+    // Epilogue, through the (now idle) ring: the wavefronts write the tile,
+    // rounded to bf16, row-major into LDS; then all threads copy the rows
+    // that exist to the staging window in 16-byte pieces.  Rows carry 16
+    // bytes of padding, so the two half-wavefronts of one LDS write (rows r
+    // and r + 4) land on different banks.
+    // In a 32x32 block, lane holds column (lane % 32), rows
+    // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v.  The
+    // empty asm statements pin each block's accumulator reads after the
+    // previous block's LDS writes, which keeps the compiler from hoisting
+    // every accumulator into VGPRs at once.
+    constexpr int OUT_COLS = SWIGLU ? BN / 2 : BN;
+    constexpr int OROWB = OUT_COLS * 2 + 16;
+    static_assert(BM * OROWB <= STAGES * STAGE_BYTES, "the output tile must fit the ring");
+    typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
+    lds_char_t *otile = (lds_char_t *)smem;
     static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
       constexpr int i = decltype(i_c)::value;
-      const int rb = (wm + i * WM) * 32;
+      const int rb = (wm + i * WM) * 32 + (lane / 32) * 4;
       if constexpr (SWIGLU) {
         static_for<FN / 2>([&](auto p_c) __attribute__((always_inline)) {
           constexpr int p = decltype(p_c)::value;
           asm volatile("" : "+a"(acc[i][2 * p]), "+a"(acc[i][2 * p + 1]));
-          const int col = n_tile * (BN / 2) + wn * (TN / 2) + p * 32 + (lane & 31);
+          const int col = wn * (TN / 2) + p * 32 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-            if (row < rows_valid) {
-              const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
-              C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(h);
-            }
+            const int row = rb + (v / 4) * 8 + (v % 4);
+            const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
+            *((lds_u16_t *)(otile + row * OROWB) + col) = f32_to_bf16_rne(h);
           }
-          __builtin_amdgcn_sched_barrier(0);
         });
       } else {
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
           asm volatile("" : "+a"(acc[i][j]));
-          const int col = n_tile * BN + wn * TN + j * 32 + (lane & 31);
+          const int col = wn * TN + j * 32 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = rb + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-            if (row < rows_valid) C[(int64_t)row * g.ldc + col] = f32_to_bf16_rne(acc[i][j][v]);
+            const int row = rb + (v / 4) * 8 + (v % 4);
+            *((lds_u16_t *)(otile + row * OROWB) + col) = f32_to_bf16_rne(acc[i][j][v]);
           }
-          __builtin_amdgcn_sched_barrier(0);
         });
       }
     });
+    __syncthreads();
+    constexpr int CHUNKS = OUT_COLS * 2 / 16;  // 16-byte pieces per row
+    u32x4 *dst = (u32x4 *)(C + (int64_t)n_tile * OUT_COLS);
+    const int ldc16 = g.ldc / 8;
+    for (int idx = tid; idx < rows_valid * CHUNKS; idx += NW * kWave) {
+      const int row = idx / CHUNKS, ch = idx % CHUNKS;
+      dst[(int64_t)row * ldc16 + ch] = *((lds_u32x4_t *)(otile + row * OROWB) + ch);
+    }
+    __syncthreads();  // the ring is read out before the next tile refills it
   };
   // one specialisation per active-block count (wavefront-uniform branch)
   static_for<FM + 1>([&](auto c) __attribute__((always_inline)) {
