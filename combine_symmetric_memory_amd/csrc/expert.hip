@@ -371,9 +371,10 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     //    (kt, 1) into buffer 1, then H0 loads of K-step kt+STAGES-1 (into
     //    the slot K-step kt-1 used, free since the previous barrier);
     //  sub-step 1: MFMAs of (kt, 1) from buffer 1; after the first row:
-    //    wait for its own share of stage kt+1, barrier (stage kt+1 complete
-    //    everywhere); items: the reads of (kt+1, 0) into buffer 0, then the
-    //    other H1 loads.
+    //    wait for its own reads of stage kt and its own share of stage kt+1,
+    //    barrier (stage kt+1 complete everywhere, stage kt's slot free from
+    //    the next K-step on); items: the reads of (kt+1, 0) into buffer 0,
+    //    then the other H1 loads.
     // Before MFMA row i, a progressive lgkmcnt wait lets the row start as
     // soon as its A fragment (and the B fragments read before it) are in.
     auto step = [&](auto st_c, int kt) __attribute__((always_inline)) {
@@ -403,9 +404,13 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         else issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, m - NRD>{}, soff);
       });
       // ---- sub-step 1
+      // The barrier of K-step kt: every wavefront's share of stage kt+1 has
+      // landed, and every wavefront's reads of stage kt are complete (the
+      // DMA that next refills stage kt's slot is issued after this barrier).
       auto sync = [&]() __attribute__((always_inline)) {
+        wait_lgkm(I0{});                        // own reads of stage kt done
         wait_vmcnt<(STAGES - 3) * LPS + H0>();  // own share of stage kt+1
-        stage_barrier();                        // stage kt+1 complete everywhere
+        stage_barrier();                        // ... for every wavefront
       };
       if constexpr (NACT == 0) sync();
       static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
