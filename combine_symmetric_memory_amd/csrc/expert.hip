@@ -75,12 +75,13 @@ __device__ __forceinline__ int rows_of(const MoeArgs &a, int e) {
   return n > 0 ? (int)n : 0;
 }
 
-// Wait until at most N vector-memory operations of this wavefront are in
-// flight (the direct-to-LDS loads included).
+// Wait until at most N vector-memory operations (the direct-to-LDS loads
+// included) / at most N LDS reads of this wavefront are in flight.  LDS
+// reads return in order, so a partial lgkmcnt wait names a prefix of them.
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8), issued through the builtin so that the
-// compiler's own wait insertion sees them.
-// Both are scheduling barriers too: no instruction moves across a wait.
+// compiler's own wait insertion sees them.  Both are scheduling barriers
+// too: no instruction moves across a wait.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -88,9 +89,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
   __builtin_amdgcn_sched_barrier(0);
 }
-__device__ __forceinline__ void wait_lgkmcnt0() {
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -158,11 +161,6 @@ template <int N, class F>
 __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
-
-// Instruction classes for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
-constexpr int kSchedDsRead = 0x100;
 
 // Full tile 256 x 256 x 32 with a 5-deep ring (32 KiB stages); the 128 x 512
 // remainder tile (40 KiB stages) with 4.  Either ring fills the 160 KiB of
@@ -344,14 +342,6 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         fa[BUF][r - FN] =
             *((lds_bf16x8_t *)(uintptr_t)fa_addr[ST][SK] + (r - FN) * WM * 32 * ROWB / 16);
     };
-    // lgkmcnt wait (in-order LDS returns): at most N reads outstanding
-    auto wait_lgkm = [&](auto n_c) __attribute__((always_inline)) {
-      constexpr int N = decltype(n_c)::value;
-      static_assert(N >= 0 && N < 16, "lgkmcnt range");
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F & ~(0xF << 8) | (N << 8));
-      __builtin_amdgcn_sched_barrier(0);
-    };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
@@ -387,7 +377,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         constexpr int i = decltype(i_c)::value;
         // new reads issued before row i: one per earlier MFMA, at most NRD
         constexpr int ISSUED = (i * FN < NRD) ? i * FN : NRD;
-        wait_lgkm(std::integral_constant<int, (NACT - 1 - i) + ISSUED>{});
+        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value, m = i * FN + j;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], acc[i][j], 0, 0, 0);
@@ -408,7 +398,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       // landed, and every wavefront's reads of stage kt are complete (the
       // DMA that next refills stage kt's slot is issued after this barrier).
       auto sync = [&]() __attribute__((always_inline)) {
-        wait_lgkm(I0{});                        // own reads of stage kt done
+        wait_lgkmcnt<0>();                      // own reads of stage kt done
         wait_vmcnt<(STAGES - 3) * LPS + H0>();  // own share of stage kt+1
         stage_barrier();                        // ... for every wavefront
       };
@@ -417,7 +407,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         constexpr int i = decltype(i_c)::value;
         // items start after row 0 (and the barrier)
         constexpr int ISSUED = (i == 0) ? 0 : (((i - 1) * FN < NRD) ? (i - 1) * FN : NRD);
-        wait_lgkm(std::integral_constant<int, (NACT - 1 - i) + ISSUED>{});
+        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value, m = (i - 1) * FN + j;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
@@ -445,7 +435,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     static_for<STAGES - 1>([&](auto p) __attribute__((always_inline)) {
       if (kt + decltype(p)::value < nk) step(p, kt + decltype(p)::value);
     });
-    wait_lgkm(I0{});
+    wait_lgkmcnt<0>();
     wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
     // every wavefront is done with the LDS before the next tile refills it
     __syncthreads();
