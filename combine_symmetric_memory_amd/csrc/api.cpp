@@ -86,6 +86,8 @@ bool shape_ok(const cco_moe_shape *s, int32_t nslots) {
   if (s->num_experts % nslots != 0) return false;
   if (s->inter < 0) return false;
   if (s->inter > 0 && (s->inter % 128 != 0 || s->hidden % 256 != 0)) return false;
+  // the expert GEMMs address one expert's weights through a 31-bit byte range
+  if (s->inter > 0 && (int64_t)4 * s->inter * s->hidden > INT32_MAX) return false;
   // int32 row and pair indices
   const int64_t eps = s->num_experts / nslots;
   const int64_t cap = (int64_t)s->max_tokens * std::min<int64_t>(s->topk, eps);

@@ -66,11 +66,14 @@ typedef struct cco_moe cco_moe;
  *   max_tokens   largest T any call will pass (sizes the receive windows)
  *   hidden       H, bf16 elements per token row; multiple of 8 (16-byte
  *                rows); with inter > 0 also a multiple of 256
- *   topk         K >= 1, experts per token
+ *   topk         K >= 1, at most 32, experts per token
  *   num_experts  E >= 1, at most 1024, a multiple of the heap's slot count
- *   inter        I, SwiGLU intermediate size, a multiple of 128;
+ *   inter        I, SwiGLU intermediate size, a multiple of 128, with one
+ *                expert's gate+up weights (4 * I * H bytes) under 2 GiB;
  *                0 selects identity experts (the expert output is the
  *                dispatched row itself and combine reads the receive window)
+ * T * K and the per-slot capacity must fit in int32.  Shapes outside these
+ * limits are rejected (-1 / 0 bytes) before anything is allocated.
  */
 typedef struct {
   int32_t max_tokens;

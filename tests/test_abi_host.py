@@ -88,6 +88,7 @@ def test_required_bytes_and_layout(capi):
     (dict(I=192), 4),             # I % 128
     (dict(H=264, I=512), 4),      # H % 256 with SwiGLU experts
     (dict(H=384, I=512), 4),      # H % 256 with SwiGLU experts
+    (dict(H=16384, I=32768), 4),  # one expert's gate+up weights reach 2 GiB
     (dict(T=-1), 4),
     (dict(), 0),
 ])
