@@ -21,7 +21,10 @@
  *   - argument errors are reported before anything is launched;
  *   - plan / dispatch / expert / combine are asynchronous on `stream` and
  *     allocate nothing; they must be issued in that order on one stream for
- *     the same T and the same idx;
+ *     the same T and the same idx.  The object's routing state, status word
+ *     and GEMM tile queues serve every pass, so two passes of one object
+ *     must not overlap on the device (use separate objects for concurrent
+ *     streams);
  *   - errors found on the device (a bad expert id, a slot overflow) go to a
  *     per-object status word that cco_moe_status reads; the next plan
  *     recomputes it.  Rows that do not fit are dropped, never written out of
