@@ -121,6 +121,56 @@ def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthr
                         "combine_per_token": t_comb, "expert_per_row": per_row}}
 
 
+def calibrate(cfg, moe, w, out, work, stream, dev, torch):
+    """Reference rates on the same GPU, each timed with L2 and MALL flushed:
+    a device-to-device copy of the dispatch's byte count, a large bf16 GEMM
+    through the vendor library (torch.matmul, hipBLASLt), and combine fed a
+    foreign expert output (the copy fallback) against the zero-copy view."""
+    flush = torch.empty(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev)
+
+    def time_ms(fn, n=5):
+        fn()
+        times = []
+        for _ in range(n):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+
+    cal = {}
+    nb = work["dispatch"]["bytes"] // 2 * 2
+    a = torch.empty(nb // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    ms = time_ms(lambda: b.copy_(a))
+    cal["d2d_copy"] = {"bytes_moved": 2 * nb, "GB_s": round(2 * nb / (ms * 1e-3) / 1e9, 1)}
+    del a, b
+    if cfg.I > 0:
+        # all of the step's rows through one expert's gate+up weights
+        M, N, K = cfg.T * cfg.K, 2 * cfg.I, cfg.H
+        x = torch.randn(M, K, device=dev).to(torch.bfloat16)
+        wt = torch.randn(K, N, device=dev).to(torch.bfloat16)   # contiguous [K, N]
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ms = time_ms(lambda: torch.matmul(x, wt, out=y))
+        cal["library_gemm"] = {"shape_MNK": [M, N, K],
+                               "TFLOP_s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        del x, wt, y
+    # combine through the copy fallback: the expert output handed over in
+    # buffers of its own (one per slot) instead of the staging views
+    foreign = [torch.empty((moe.cap, cfg.H), dtype=torch.bfloat16, device=dev)
+               for _ in range(cfg.S)]
+    ms_view = time_ms(lambda: moe.combine(w, out=out, stream=stream))
+    ms_copy = time_ms(lambda: moe.combine(w, out=out, expert_out=foreign, stream=stream))
+    cal["combine_copy_fallback"] = {"view_ms": round(ms_view, 4), "foreign_ms": round(ms_copy, 4),
+                                    "extra_ms": round(ms_copy - ms_view, 4)}
+    del foreign, flush
+    return cal
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +300,10 @@ def main():
         roofline = dict(kernel=dom, bound="hbm", **hbm)
     roofline["traffic"] = profiled_traffic(cfg.name, dom)
 
+    # ---- calibrations: context for the stage rates, outside the step ----
+    calibration = calibrate(cfg, moe, w, out, work, stream, dev, torch)
+    log("calibration", json.dumps(calibration))
+
     dc_bytes = stages["dispatch"]["alg_bytes"] + stages["combine"]["alg_bytes"]
     dc_ms = stages["dispatch"]["avg_ms"] + stages["combine"]["avg_ms"]
     summary = {"dispatch_combine_GB_s": round(dc_bytes / (dc_ms * 1e-3) / 1e9, 1),
@@ -306,6 +360,7 @@ def main():
         "summary": summary,
         "stages": stages,
         "roofline": roofline,
+        "calibration": calibration,
         "cpu_baseline": cpu,
     }
     heap.destroy()
