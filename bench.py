@@ -121,7 +121,7 @@ def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthr
                         "combine_per_token": t_comb, "expert_per_row": per_row}}
 
 
-def calibrate(cfg, moe, w, out, work, stream, dev, torch):
+def calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert=None):
     """Reference rates on the same GPU, each timed with L2 and MALL flushed:
     a device-to-device copy of the dispatch's byte count, a large bf16 GEMM
     through the vendor library (torch.matmul, hipBLASLt), and combine fed a
@@ -159,6 +159,22 @@ def calibrate(cfg, moe, w, out, work, stream, dev, torch):
         cal["library_gemm"] = {"shape_MNK": [M, N, K],
                                "TFLOP_s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
         del x, wt, y
+    if per_expert is not None:
+        # the gate/up projection as one vendor GEMM per expert, on the same
+        # rows (gathered beforehand) and weights: the straightforward
+        # alternative to the grouped kernel
+        xs, w13 = per_expert
+        ys = [torch.empty((xe.shape[0], 2 * cfg.I), dtype=torch.bfloat16, device=dev)
+              for _, xe in xs]
+
+        def loop():
+            for (e, xe), ye in zip(xs, ys):
+                torch.matmul(xe, w13[e].t(), out=ye)
+        ms = time_ms(loop, n=3)
+        fl = sum(2.0 * xe.shape[0] * 2 * cfg.I * cfg.H for _, xe in xs)
+        cal["library_gemm_per_expert_gate_up"] = {"experts": len(xs), "ms": round(ms, 4),
+                                                  "TFLOP_s": round(fl / (ms * 1e-3) / 1e12, 1)}
+        del ys
     # combine through the copy fallback: the expert output handed over in
     # buffers of its own (one per slot) instead of the staging views
     foreign = [torch.empty((moe.cap, cfg.H), dtype=torch.bfloat16, device=dev)
@@ -301,7 +317,23 @@ def main():
     roofline["traffic"] = profiled_traffic(cfg.name, dom)
 
     # ---- calibrations: context for the stage rates, outside the step ----
-    calibration = calibrate(cfg, moe, w, out, work, stream, dev, torch)
+    per_expert = None
+    if cfg.I > 0:
+        # each expert's rows, in its receive order, as a contiguous tensor
+        order = np.argsort(idx_np.ravel(), kind="stable")
+        eid = idx_np.ravel()[order]
+        xs = []
+        start = 0
+        for e in range(cfg.E):
+            n = int(counts[e])
+            if n:
+                rows = torch.from_numpy((order[start:start + n] // cfg.K).astype(np.int64)).to(dev)
+                xs.append((e, x.index_select(0, rows)))
+            start += n
+        assert start == len(eid)
+        per_expert = (xs, w13)
+    calibration = calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert)
+    del per_expert
     log("calibration", json.dumps(calibration))
 
     dc_bytes = stages["dispatch"]["alg_bytes"] + stages["combine"]["alg_bytes"]
