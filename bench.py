@@ -56,19 +56,31 @@ def stage_work(cfg, active_experts=None):
     return w
 
 
+def code_digest(path):
+    """sha256 of a C++/HIP source with its // comments, trailing blanks and
+    empty lines removed: a change to the comments keeps the digest."""
+    import hashlib
+    import re
+    lines = []
+    for line in open(path).read().split("\n"):
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def profiled_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if there is none for this workload or the expert kernel
-    source changed since the counters were taken."""
-    import hashlib
+    summary, or None if there is none for this workload or the expert kernel's
+    code changed since the counters were taken."""
     import re
     path = os.path.join(ROOT, "profiles", "traffic_%s.md" % workload)
     src = os.path.join(ROOT, "combine_symmetric_memory_amd", "csrc", "expert.hip")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"expert_source_sha256: ([0-9a-f]+)", text)
-    if not m or m.group(1) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    m = re.search(r"expert_code_sha256: ([0-9a-f]+)", text)
+    if not m or m.group(1) != code_digest(src):
         return None
     m = re.search(r"traffic_bytes_per_launch %s: (\d+)" % re.escape(kernel), text)
     return int(m.group(1)) if m else None

@@ -18,10 +18,9 @@
 // m-tiles of one (expert, n-tile) reuse one weight panel, the n-tiles of one
 // expert reuse its receive rows.
 //
-// Inside a tile, 8 wavefronts in two groups alternate between a memory
-// phase (LDS fragment reads, then direct global -> LDS loads of a later
-// K-step into a ring of stages) and a compute phase (MFMAs only); see
-// run_tile.
+// Inside a tile, 4 wavefronts (one per SIMD) interleave their MFMAs with
+// LDS fragment reads and with direct global -> LDS loads of a later K-step
+// into a ring of stages; see run_tile.
 //
 // Gate/up fusion: the B tile interleaves 32-row blocks of the gate and up
 // projections so that each wavefront holds, for the same 32 intermediate
