@@ -135,9 +135,11 @@ def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthr
 
 def calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert=None):
     """Reference rates on the same GPU, each timed with L2 and MALL flushed:
-    a device-to-device copy of the dispatch's byte count, a large bf16 GEMM
-    through the vendor library (torch.matmul, hipBLASLt), and combine fed a
-    foreign expert output (the copy fallback) against the zero-copy view."""
+    a device-to-device copy of the dispatch's byte count, torch kernels with
+    the byte mixes of dispatch and combine, a large bf16 GEMM through the
+    vendor library (torch.matmul, hipBLASLt) and one vendor GEMM per expert,
+    and combine fed a foreign expert output (the copy fallback) against the
+    zero-copy view."""
     flush = torch.empty(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev)
 
     def time_ms(fn, n=5):
@@ -161,6 +163,22 @@ def calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert=None):
     ms = time_ms(lambda: b.copy_(a))
     cal["d2d_copy"] = {"bytes_moved": 2 * nb, "GB_s": round(2 * nb / (ms * 1e-3) / 1e9, 1)}
     del a, b
+    # the byte mixes of dispatch and combine through torch's own kernels:
+    # every token row written K times (a broadcast copy into [K, T, H]), and
+    # the K rows of every token summed (a reduction over [T, K, H])
+    T, H, K = cfg.T, cfg.H, cfg.K
+    xa = torch.empty((T, H), dtype=torch.bfloat16, device=dev).fill_(1.0)
+    rep = torch.empty((K, T, H), dtype=torch.bfloat16, device=dev)
+    ms = time_ms(lambda: rep.copy_(xa.unsqueeze(0).expand(K, T, H)))
+    mixed = 2 * T * H * (1 + K)
+    cal["library_broadcast_x%d" % K] = {"bytes_moved": mixed,
+                                        "GB_s": round(mixed / (ms * 1e-3) / 1e9, 1)}
+    red = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    rows = rep.view(T, K, H)
+    ms = time_ms(lambda: torch.sum(rows, dim=1, out=red))
+    cal["library_sum_of_%d_rows" % K] = {"bytes_moved": mixed,
+                                         "GB_s": round(mixed / (ms * 1e-3) / 1e9, 1)}
+    del xa, rep, red, rows
     if cfg.I > 0:
         # all of the step's rows through one expert's gate+up weights
         M, N, K = cfg.T * cfg.K, 2 * cfg.I, cfg.H
