@@ -148,6 +148,26 @@ def test_generic_topk_and_limits(ccm, orc, K, E, S, T):
     heap.destroy()
 
 
+@pytest.mark.parametrize("H,I,E,S,K,T", [
+    (768, 384, 6, 3, 2, 300),     # odd column-tile counts in both GEMMs (no 128-row tiles)
+    (256, 128, 4, 2, 1, 700),     # down: 4 K-steps, fewer than the ring holds; top-1
+    (1280, 640, 8, 8, 4, 256),    # one expert per slot, five column tiles each
+    (512, 1024, 2, 1, 2, 1000),   # a single slot; four m-tiles per expert
+    (72, 0, 8, 2, 3, 50),         # identity: 9 vectors per row, most lanes idle
+    (8200, 0, 4, 4, 2, 33),       # identity: rows longer than one dispatch chunk
+])
+def test_shape_sweep(ccm, orc, H, I, E, S, K, T):
+    cfg = get_config("tiny").with_(name="sweep", H=H, I=I, E=E, S=S, K=K, T=T)
+    say("case: sweep H=%d I=%d E=%d S=%d K=%d T=%d" % (H, I, E, S, K, T))
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    out, code = run_path(moe, c)
+    assert code == ccm.CCO_OK
+    _check_all_stages(orc, moe, c, out)
+    assert all((g == 0xA5).all() for g in read_guards(moe)), "a window overran its guard bytes"
+    heap.destroy()
+
+
 @pytest.mark.parametrize("T", [0, 1, 37, 127])
 def test_ragged_token_counts(ccm, orc, T):
     cfg = get_config("tiny")
