@@ -271,10 +271,22 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   const int64_t npairs = (int64_t)shape->max_tokens * shape->topk;
   m->max_plan_blocks = plan_blocks(npairs);
   const int E = shape->num_experts;
+  if (hipDeviceGetAttribute(&m->num_cus, hipDeviceAttributeMultiprocessorCount, heap->device) !=
+          hipSuccess ||
+      m->num_cus <= 0) {
+    delete m;
+    return CCO_ERR_HIP;
+  }
   // routing state: pos, eid, counts, expert_off, slot_total, status, ticket,
-  // GEMM tile queues, hist
-  const size_t n_i32 = (size_t)npairs * 2 + (size_t)E * 2 + (size_t)m->S + 2 +
-                       2 * (cco::kNumXcd + 1) + (size_t)m->max_plan_blocks * (E + 1);
+  // GEMM tile queues, split-tile descriptors, hist, and (with experts) the
+  // split tiles' partial sums, 256-byte aligned
+  const int nwg = cco::gemm_workgroups(m->num_cus);
+  const size_t n_desc = (size_t)(nwg / 2) * cco::kSplitDescInts;
+  const size_t n_head = (size_t)npairs * 2 + (size_t)E * 2 + (size_t)m->S + 2 +
+                        4 * (cco::kNumXcd + 1) + n_desc + (size_t)m->max_plan_blocks * (E + 1);
+  const size_t ws_at = (n_head + 63) / 64 * 64;
+  const size_t n_ws = shape->inter > 0 ? (size_t)nwg * cco::kSplitTileFloats : 0;
+  const size_t n_i32 = ws_at + n_ws;
   void *st = nullptr;
   hipError_t err = hipMalloc(&st, std::max<size_t>(n_i32, 1) * sizeof(int32_t));
   if (err != hipSuccess) {
@@ -308,8 +320,10 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   a.slot_total = p;        p += m->S;
   a.status = p;            p += 1;
   a.ticket = p;            p += 1;
-  a.gemm_queue = p;        p += 2 * (cco::kNumXcd + 1);
+  a.gemm_queue = p;        p += 4 * (cco::kNumXcd + 1);
+  a.split_desc = p;        p += n_desc;
   a.hist = p;
+  a.split_ws = n_ws ? (float *)((int32_t *)st + ws_at) : nullptr;
 
   // guard bytes after every window of every slot
   const uint64_t wo[4] = {m->lay.disp_x, m->lay.disp_meta, m->lay.hbuf, m->lay.out_tok};
@@ -322,12 +336,6 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
         free_moe(m);
         return CCO_ERR_HIP;
       }
-  if (hipDeviceGetAttribute(&m->num_cus, hipDeviceAttributeMultiprocessorCount, heap->device) !=
-          hipSuccess ||
-      m->num_cus <= 0) {
-    free_moe(m);
-    return CCO_ERR_HIP;
-  }
   if (hipDeviceSynchronize() != hipSuccess) {
     free_moe(m);
     return CCO_ERR_HIP;
@@ -395,9 +403,12 @@ int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *st
   hipStream_t st = (hipStream_t)stream;
   if (m->planned_T == 0) return CCO_OK;
   MoeArgs a = m->args;
-  int rc = timed_launch(m, 3, st, [&] { return cco::launch_expert_gate_up(a, w13, m->num_cus, st); });
+  const int32_t T = m->planned_T;
+  int rc = timed_launch(m, 3, st,
+                        [&] { return cco::launch_expert_gate_up(a, w13, T, m->num_cus, st); });
   if (rc != CCO_OK) return rc;
-  return timed_launch(m, 4, st, [&] { return cco::launch_expert_down(a, w2, m->num_cus, st); });
+  return timed_launch(m, 4, st,
+                      [&] { return cco::launch_expert_down(a, w2, T, m->num_cus, st); });
 }
 
 void *cco_moe_dispatch_view(cco_moe *m, int32_t slot) {

@@ -44,8 +44,17 @@ struct MoeArgs {
   int32_t *status;     // [1]
   int32_t *hist;       // [plan blocks][E + 1] scratch
   int32_t *ticket;     // [1] scratch, zero between plans
-  int32_t *gemm_queue; // [2][kNumXcd + 1] tile queues of the two expert GEMMs, zero between launches
+  int32_t *gemm_queue; // [4][kNumXcd + 1] tile queues: the two expert GEMMs, then their split-tile tails; zero between launches
+  float *split_ws;     // [gemm_workgroups][kSplitTileFloats] partial sums of split GEMM tiles
+  int32_t *split_desc; // [gemm_workgroups / 2][kSplitDescInts] split tiles, zero between launches
 };
+
+// The expert GEMMs run one workgroup per CU, in whole XCDs.
+inline int gemm_workgroups(int num_cus) { return ((num_cus + kNumXcd - 1) / kNumXcd) * kNumXcd; }
+// fp32 accumulators of one GEMM tile (256 x 256, or 128 x 512), and the
+// words describing one tile whose K-steps were split over workgroups.
+constexpr int kSplitTileFloats = 256 * 256;
+constexpr int kSplitDescInts = 8;
 
 // Address of byte `off` of window `win_off` in slot `s`:
 // base + s * stride + win_off + off.
@@ -66,10 +75,11 @@ hipError_t launch_combine(const MoeArgs &a, uint64_t src_win, const float *w,
 hipError_t launch_copy_in(const MoeArgs &a, int32_t slot, const uint16_t *src,
                           uint64_t dst_win, hipStream_t st);
 
-// Expert GEMMs.  `num_cus` sizes the persistent grids.
-hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int num_cus,
+// Expert GEMMs of the T planned tokens.  `num_cus` sizes the persistent
+// grids.
+hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int32_t T, int num_cus,
                                  hipStream_t st);
-hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int num_cus,
+hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int32_t T, int num_cus,
                               hipStream_t st);
 
 }  // namespace cco

@@ -63,6 +63,9 @@ struct GemmDesc {
   int32_t ntiles;        // tiles along N
   int32_t up_off;        // gate/up: first row of the up projection (= I)
   int32_t *queue;        // [kNumXcd] next-tile counters + [1] exit counter
+  int32_t allow_split;   // nonzero: the tail and fixup launches follow this GEMM
+  float *split_ws;       // fp32 partial sums of split tiles: one slot per workgroup
+  int32_t *split_desc;   // [workgroups / 2][kSplitDescInts] split tiles, kind 0 = free
 };
 
 // Rows of expert e that fit its slot (a slot overflow is reported by the
@@ -169,6 +172,18 @@ constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 5, kStagesHalf = 4;
 // Wavefronts per workgroup: one per SIMD.
 constexpr int kGemmWaves = 4;
 
+// Split of a short last round: a tile cut into K-ranges keeps at least this
+// many K-steps per range.  Each range's fp32 partial sums take one
+// workspace slot of kSplitTileFloats (either tile shape has that many
+// accumulators).
+constexpr int kMinSplitSteps = 8;
+// Only GEMMs of fewer rounds than this split their last one: with more,
+// the short round is a small part of the time, and the dynamic hand-out
+// already fills much of it.
+constexpr int kSplitMaxRounds = 4;
+static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTileFloats,
+              "a workspace slot holds one tile's accumulators");
+
 // Tile: BM rows x BN columns of one expert on 4 wavefronts, one per SIMD,
 // each owning a 128 x 128 block of the output as 4 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16 with the accumulators in AGPRs.  Wavefront w sits
@@ -193,11 +208,15 @@ constexpr int kGemmWaves = 4;
 //
 // n_tile counts BN-wide column tiles (for gate/up: BN/2 intermediate
 // columns, gate and up interleaved in 32-row blocks); rows [row0, row0 +
-// rows_valid) of expert e are computed.  Every wavefront of the workgroup
-// calls this with the same arguments.
+// rows_valid) of expert e are computed over the nkt K-steps from kb on.
+// With part == nullptr the result goes to the expert's output rows;
+// otherwise the fp32 sums of this K-range are written to part, row-major
+// [BM][BN] in the accumulators' column order.  Every wavefront of the
+// workgroup calls this with the same arguments.
 template <int BM, int BN, int STAGES, bool SWIGLU>
 __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
-                                         int n_tile, int row0, int rows_valid, int lag) {
+                                         int n_tile, int row0, int rows_valid, int lag, int kb,
+                                         int nkt, float *part) {
   constexpr int BK = kBK;
   constexpr int NW = kGemmWaves;
   constexpr int WM = BM / 128;          // wavefront rows
@@ -233,9 +252,10 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   row0 = uniform(row0);
   rows_valid = uniform(rows_valid);
   lag = uniform(lag);
+  kb = uniform(kb);
   const int slot = e / a.eps;
   const int64_t grow0 = (int64_t)uniform(a.expert_off[e]) + row0;
-  const int nk = g.kdim / BK;
+  const int nk = uniform(nkt);
 
   const char *A = uniform(slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2));
   const char *B = uniform((const char *)(g.w + (int64_t)e * g.w_estride));
@@ -293,7 +313,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
 
   // load q (0 .. LPS-1: A loads, then B loads) of this wavefront's share of
   // K-step kt (the tail re-loads the last one) into ring stage ST; K-steps
-  // run from lag, wrapping.  Scalar offsets only.
+  // run from kb + lag, wrapping inside [kb, kb + nk).  Scalar offsets only.
   auto issue_load = [&](auto st_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value, q = decltype(q_c)::value;
     char *sbase = smem + ST * STAGE_BYTES;
@@ -305,7 +325,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   auto k_offset = [&](int kt) __attribute__((always_inline)) {
     int kc = (kt < nk ? kt : nk - 1) + lag;
     if (kc >= nk) kc -= nk;
-    return (uint32_t)kc * ROWB;
+    return (uint32_t)(kb + kc) * ROWB;
   };
 
   // this wavefront's blocks (wm + WM i) holding rows: a prefix i < nact
@@ -439,6 +459,24 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     // every wavefront is done with the LDS before the next tile refills it
     __syncthreads();
 
+    if (part != nullptr) {
+      // partial sums of a K-range: straight from the accumulators, 32
+      // consecutive floats of two rows per store
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        const int rb = (wm + i * WM) * 32 + (lane / 32) * 4;
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          asm volatile("" : "+a"(acc[i][j]));
+          const int col = wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            part[(rb + (v / 4) * 8 + (v % 4)) * BN + col] = acc[i][j][v];
+        });
+      });
+      return;
+    }
+
     // Epilogue, through the (now idle) ring: the wavefronts write the tile,
     // rounded to bf16, row-major into LDS; then all threads copy the rows
     // that exist to the staging window in 16-byte pieces.  Rows carry 16
@@ -524,7 +562,10 @@ __device__ __forceinline__ ExpertTiles expert_tiles(int rows, int ntl) {
 // expert: n-tile major, m-tile minor, so the m-tiles of one weight panel run
 // side by side; with a half remainder, the pair of column tiles (2j, 2j+1)
 // lists its full m-tiles and then the remainder tile j that spans both.
-template <bool SWIGLU>
+// TAIL = false runs the whole tiles; TAIL = true, launched after it, the
+// K-ranges of the split tiles (each instantiation keeps only its own
+// epilogue, so the main one's register allocation is not disturbed).
+template <bool SWIGLU, bool TAIL>
 __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
   constexpr int NT = kGemmWaves * kWave;
   // The ring of the running tile shape takes all of the LDS.  Between tiles
@@ -594,13 +635,32 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   const int t_end = (int)((int64_t)total * (xcd + 1) / kNumXcd);
   const int nk = g.kdim / kBK;
 
+  // The last round of an XCD's range is short when its U tiles leave a
+  // small remainder R over the XCD's W workgroups.  Then the last R tiles
+  // are cut into P ranges of K-steps each, which fills that round; every
+  // range writes fp32 partial sums, and split_fixup_kernel adds a tile's
+  // ranges in order once all of them are done.  The counter hands out
+  // units: the U - R whole tiles (main launch), or the R * P ranges, tile
+  // by tile (tail launch).
+  const int W = gridDim.x / kNumXcd;
+  const int U = t_end - t_begin;
+  const int R = U % W;
+  int P = (g.allow_split && U < kSplitMaxRounds * W && R > 0 && 2 * R <= W)
+              ? min(W / R, nk / kMinSplitSteps)
+              : 1;
+  if (P < 2) P = 1;
+  const int n_whole = P > 1 ? U - R : U;
+  const int n_units = TAIL ? (P > 1 ? R * P : 0) : n_whole;
+
   for (;;) {
-    if (tid == 0) scratch[0] = t_begin + atomicAdd(&g.queue[xcd], 1);
+    if (tid == 0) scratch[0] = atomicAdd(&g.queue[xcd], 1);
     __syncthreads();
-    // the tile index and everything derived from it are wavefront-uniform:
-    // keep them in scalar registers, so that per-K-step offsets stay scalar
-    const int L = uniform(scratch[0]);
-    if (L >= t_end) break;
+    // the unit and everything derived from it are wavefront-uniform: keep
+    // them in scalar registers, so that per-K-step offsets stay scalar
+    const int u = uniform(scratch[0]);
+    if (u >= n_units) break;
+    const int v = u;                     // tail: the unit is a K-range of a split tile
+    const int L = t_begin + (TAIL ? n_whole + v / P : u);
     // the thread owning expert e with L in [pre, pre + loc) posts (e, L - pre)
 #pragma unroll
     for (int q = 0; q < PER; ++q)
@@ -614,30 +674,58 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
     __syncthreads();  // scratch read everywhere before the ring refills
     const int rows = uniform(rows_of(a, e));
     const ExpertTiles et = expert_tiles(rows, ntl);
+    int kind, n_tile, m_tile, row0, rows_valid;
+    if (et.half && r % (2 * et.q + 1) == 2 * et.q) {
+      kind = 2;
+      n_tile = r / (2 * et.q + 1);
+      m_tile = et.q;
+      row0 = et.q * kBM;
+      rows_valid = et.rem;
+    } else {
+      if (et.half) {
+        const int per = 2 * et.q + 1;
+        const int j = r / per;
+        const int rr = r - j * per;
+        n_tile = 2 * j + rr / et.q;
+        m_tile = rr % et.q;
+      } else {
+        const int mt_e = et.q + (et.rem > 0);
+        n_tile = r / mt_e;
+        m_tile = r - n_tile * mt_e;
+      }
+      kind = 1;
+      row0 = m_tile * kBM;
+      rows_valid = min(kBM, rows - row0);
+    }
+    // K-range of this unit, and where its partial sums go
+    int kb = 0, nkt = nk;
+    float *part = nullptr;
+    if (TAIL) {
+      const int piece = v % P;
+      kb = piece * nk / P;
+      nkt = (piece + 1) * nk / P - kb;
+      part = g.split_ws + (int64_t)(xcd * W + v) * kSplitTileFloats;
+      if (piece == 0 && tid == 0) {
+        int32_t *d = g.split_desc + (xcd * (W / 2) + v / P) * kSplitDescInts;
+        d[0] = kind;
+        d[1] = e;
+        d[2] = n_tile;
+        d[3] = row0;
+        d[4] = rows_valid;
+        d[5] = P;
+        d[6] = xcd * W + v;  // workspace slot of the first range
+      }
+    }
     // Tiles sharing a weight panel or receive rows run side by side on one
     // XCD; rotating the K order by a small tile-dependent lag keeps them from
     // missing the same L2 lines at the same moment.
-    if (et.half) {
-      const int per = 2 * et.q + 1;
-      const int j = r / per;
-      const int rr = r - j * per;
-      if (rr < 2 * et.q) {
-        const int n_tile = 2 * j + rr / et.q;
-        const int m_tile = rr % et.q;
-        run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, m_tile * kBM, kBM,
-                                            (n_tile % 8 + m_tile % 4) % nk);
-      } else {
-        run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU>(a, g, smem, e, j, et.q * kBM, et.rem,
-                                                        (j % 8 + et.q % 4) % nk);
-      }
-    } else {
-      const int mt_e = et.q + (et.rem > 0);
-      const int n_tile = r / mt_e;
-      const int m_tile = r - n_tile * mt_e;
-      run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, m_tile * kBM,
-                                          min(kBM, rows - m_tile * kBM),
-                                          (n_tile % 8 + m_tile % 4) % nk);
-    }
+    const int lag = (n_tile % 8 + m_tile % 4) % nkt;
+    if (kind == 2)
+      run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid,
+                                                      lag, kb, nkt, part);
+    else
+      run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid, lag, kb, nkt,
+                                          part);
   }
   // the last workgroup out has seen every counter exhausted: rearm them for
   // the next launch (ordered by the stream)
@@ -647,21 +735,117 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   }
 }
 
+// Sums the K-ranges of each split tile in range order (fp32), applies the
+// epilogue of the GEMM (SwiGLU for gate/up) and writes the bf16 rows that
+// exist.  kFixBands workgroups share a tile, one band of rows each, four
+// output columns per thread and 16-byte loads; the last band to finish
+// frees the tile's descriptor for the next launch.  Runs on the GEMM's
+// stream after it, so every range's partial sums are visible.
+constexpr int kFixBands = 16;
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void split_fixup_kernel(MoeArgs a, GemmDesc g) {
+  int32_t *d = g.split_desc + (blockIdx.x / kFixBands) * kSplitDescInts;
+  const int band = blockIdx.x % kFixBands;
+  const int kind = uniform(d[0]);
+  if (kind == 0) return;
+  const int e = uniform(d[1]);
+  const int n_tile = uniform(d[2]);
+  const int row0 = uniform(d[3]);
+  const int rows = uniform(d[4]);
+  const int P = uniform(d[5]);
+  const int slot0 = uniform(d[6]);
+  const int BM = kind == 1 ? kBM : kBM / 2;
+  const int BN = kind == 1 ? kBN : 2 * kBN;
+  const int TN = BN / (kGemmWaves / (BM / 128));  // accumulator columns per wavefront
+  const int out_cols = SWIGLU ? BN / 2 : BN;
+  const float *ws = g.split_ws + (int64_t)slot0 * kSplitTileFloats;
+  const int64_t grow0 = (int64_t)a.expert_off[e] + row0;
+  uint16_t *C = (uint16_t *)slot_addr(a, e / a.eps, g.c_win, (uint64_t)grow0 * g.ldc * 2) +
+                (int64_t)n_tile * out_cols;
+  // four consecutive accumulator columns, summed over the ranges in order
+  auto sum4 = [&](int row, int col) __attribute__((always_inline)) {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int p = 0; p < P; ++p) {
+      const float4 v = *(const float4 *)(ws + (int64_t)p * kSplitTileFloats + row * BN + col);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    return acc;
+  };
+  const int rpb = BM / kFixBands;
+  const int r0 = band * rpb;
+  const int nr = min(rows - r0, rpb);
+  const int g4 = out_cols / 4;
+  for (int idx = threadIdx.x; idx < nr * g4; idx += blockDim.x) {
+    const int row = r0 + idx / g4, oc = (idx % g4) * 4;
+    float y[4];
+    if (SWIGLU) {
+      // output column oc of wavefront column wnb: gate in accumulator
+      // block 2 (rr / 32), up in the block after it
+      const int wnb = oc / (TN / 2), rr = oc % (TN / 2);
+      const int cg = wnb * TN + (rr / 32) * 64 + rr % 32;
+      const float4 gs = sum4(row, cg), us = sum4(row, cg + 32);
+      y[0] = silu(gs.x) * us.x;
+      y[1] = silu(gs.y) * us.y;
+      y[2] = silu(gs.z) * us.z;
+      y[3] = silu(gs.w) * us.w;
+    } else {
+      const float4 ys = sum4(row, oc);
+      y[0] = ys.x;
+      y[1] = ys.y;
+      y[2] = ys.z;
+      y[3] = ys.w;
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16);
+    *(uint2 *)(C + (int64_t)row * g.ldc + oc) = o;
+  }
+  // every band has read the descriptor before the last one clears it
+  __syncthreads();
+  if (threadIdx.x == 0 && atomicAdd(&d[7], 1) == kFixBands - 1) {
+    d[7] = 0;
+    d[0] = 0;
+  }
+}
+
 constexpr size_t kGemmLds =
     std::max((size_t)kStages * (kBM + kBN) * kBK * 2,
              (size_t)kStagesHalf * (kBM / 2 + 2 * kBN) * kBK * 2);
 
+// The tail and fixup launches follow only when the GEMM may split, that is
+// when it can have fewer than kSplitMaxRounds rounds: every expert's rows R
+// take at least ntiles * R / kBM tiles, so T * K routed rows take at least
+// ntiles * T * K / kBM.
 template <bool SWIGLU>
-hipError_t launch_gemm(const MoeArgs &a, const GemmDesc &g, int num_cus, hipStream_t st) {
-  int nwg = ((num_cus + kNumXcd - 1) / kNumXcd) * kNumXcd;  // one workgroup per CU
-  auto kern = grouped_gemm_kernel<SWIGLU>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kGemmWaves * kWave), kGemmLds, st, a, g);
+hipError_t launch_gemm(const MoeArgs &a, GemmDesc g, int32_t T, int num_cus, hipStream_t st) {
+  const int nwg = gemm_workgroups(num_cus);
+  const int64_t min_tiles = (int64_t)g.ntiles * T * a.K / kBM;
+  g.allow_split = min_tiles < (int64_t)kSplitMaxRounds * nwg;
+  hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, false>), dim3(nwg), dim3(kGemmWaves * kWave),
+                     kGemmLds, st, a, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !g.allow_split) return err;
+  // the split tiles' K-ranges, with counters of their own
+  GemmDesc gt = g;
+  gt.queue = g.queue + 2 * (kNumXcd + 1);
+  hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, true>), dim3(nwg), dim3(kGemmWaves * kWave),
+                     kGemmLds, st, a, gt);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // kFixBands workgroups per descriptor (at most half an XCD's workgroups
+  // per XCD); those of free descriptors return at once
+  hipLaunchKernelGGL(split_fixup_kernel<SWIGLU>, dim3(nwg / 2 * kFixBands), dim3(256), 0, st, a,
+                     g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int num_cus,
+hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int32_t T, int num_cus,
                                  hipStream_t st) {
   GemmDesc g;
   g.a_win = a.off_disp_x;
@@ -676,10 +860,12 @@ hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int num_
   g.ntiles = a.I / (kBN / 2);
   g.up_off = a.I;
   g.queue = a.gemm_queue;
-  return launch_gemm<true>(a, g, num_cus, st);
+  g.split_ws = a.split_ws;
+  g.split_desc = a.split_desc;
+  return launch_gemm<true>(a, g, T, num_cus, st);
 }
 
-hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int num_cus,
+hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int32_t T, int num_cus,
                               hipStream_t st) {
   GemmDesc g;
   g.a_win = a.off_hbuf;
@@ -694,7 +880,9 @@ hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int num_cus,
   g.ntiles = a.H / kBN;
   g.up_off = 0;
   g.queue = a.gemm_queue + kNumXcd + 1;
-  return launch_gemm<false>(a, g, num_cus, st);
+  g.split_ws = a.split_ws;
+  g.split_desc = a.split_desc;
+  return launch_gemm<false>(a, g, T, num_cus, st);
 }
 
 }  // namespace cco

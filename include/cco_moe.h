@@ -142,7 +142,9 @@ int cco_moe_layout_of(const cco_moe_shape *shape, int32_t nslots, cco_moe_layout
 
 /* Carve the windows of one MoE layer out of every slot of `heap`, at the
  * heap's next free offset (the same in every slot), and allocate its
- * routing state.  The heap owns the result.  [blog] "Zero-copy MoE
+ * routing state: the plan's per-pair arrays and scratch, and, with experts
+ * (inter > 0), a workspace for the expert GEMMs' split tiles of 256 KiB per
+ * compute unit (64 MiB on MI355X).  The heap owns the result.  [blog] "Zero-copy MoE
  * dispatch -> expert -> combine": the op object is built on the
  * communicator and every intermediate it hands out is a view of symmetric
  * memory.

@@ -153,6 +153,9 @@ def test_generic_topk_and_limits(ccm, orc, K, E, S, T):
     (256, 128, 4, 2, 1, 700),     # down: 4 K-steps, fewer than the ring holds; top-1
     (1280, 640, 8, 8, 4, 256),    # one expert per slot, five column tiles each
     (512, 1024, 2, 1, 2, 1000),   # a single slot; four m-tiles per expert
+    (256, 2048, 2, 2, 1, 300),    # down: one tile per expert cut into 8 K-ranges
+    (2048, 128, 2, 2, 1, 300),    # gate/up: one tile per expert cut into 8 K-ranges
+    (512, 1024, 4, 2, 1, 400),    # 128 x 512 remainder tiles cut into K-ranges
     (72, 0, 8, 2, 3, 50),         # identity: 9 vectors per row, most lanes idle
     (8200, 0, 4, 4, 2, 33),       # identity: rows longer than one dispatch chunk
 ])
