@@ -189,8 +189,10 @@ int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights,
  *   w13  device bf16 [E][2I][H]: rows 0..I-1 gate, rows I..2I-1 up
  *   w2   device bf16 [E][H][I]
  * (both K-contiguous, like nn.Linear.weight).  Row counts are read on the
- * device; nothing is copied to the host.  With inter == 0 this is a no-op
- * (identity experts; w13 and w2 may be NULL). */
+ * device; nothing is copied to the host.  Results are deterministic for a
+ * given routing on a given device: in GEMMs of few tile rounds the last
+ * tiles sum their K-steps in ranges, added in range order.  With
+ * inter == 0 this is a no-op (identity experts; w13 and w2 may be NULL). */
 int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *stream);
 
 /* Receive window (recv_x) of `slot`: DISP_X base, [cap][H] bf16; rows
