@@ -175,6 +175,39 @@ void orc_dispatch(const uint16_t *x, const float *w, const int32_t *idx,
   }
 }
 
+/*
+ * Dispatch of tokens the caller has already quantized to 8 bits, with their
+ * scales ([blog] "Zero-copy MoE dispatch": the op's dispatch takes the
+ * tokens, their routing weights, their scales and the expert ids, and hands
+ * back the received tokens, weights and scales).  The pages fix no layout
+ * for the received scales; this library's reading: a receive row keeps its
+ * 2H bytes, the token's H bytes fill the first half and its ns fp32 scales
+ * the 4*ns bytes after them; the rest of the row is not written.
+ *
+ * rows is [S][cap][2H] bytes; meta_* as in orc_dispatch.
+ */
+void orc_dispatch_fp8(const uint8_t *x, const float *scales, int32_t ns, const float *w,
+                      const int32_t *idx, const int32_t *pos, int64_t T, int32_t K,
+                      int64_t H, int32_t E, int32_t S, int64_t cap, uint8_t *rows,
+                      int32_t *meta_src, float *meta_w, int32_t *meta_e) {
+  int32_t eps = E / S;
+  int64_t t;
+  int32_t j;
+  for (t = 0; t < T; ++t) {
+    for (j = 0; j < K; ++j) {
+      int64_t f = t * K + j;
+      int32_t e = idx[f];
+      int64_t row = (int64_t)(e / eps) * cap + pos[f];
+      uint8_t *r = rows + row * 2 * H;
+      memcpy(r, x + t * H, (size_t)H);
+      memcpy(r + H, scales + t * ns, (size_t)ns * sizeof(float));
+      meta_src[row] = (int32_t)f;
+      meta_w[row] = w[f];
+      meta_e[row] = e;
+    }
+  }
+}
+
 /* --------------------------------------------------------------- expert --- */
 
 /*

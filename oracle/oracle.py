@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.orc_plan.restype = ctypes.c_int
         L.orc_dispatch.argtypes = [P, P, P, P, i64, i32, i64, i32, i32, i64, P, P, P, P]
         L.orc_dispatch.restype = None
+        L.orc_dispatch_fp8.argtypes = [P, P, i32, P, P, P, i64, i32, i64, i32, i32, i64, P, P, P, P]
+        L.orc_dispatch_fp8.restype = None
         L.orc_swiglu_rows.argtypes = [P, i64, i64, i64, P, P, P, ctypes.c_int]
         L.orc_swiglu_rows.restype = None
         L.orc_combine_tokens.argtypes = [P, P, P, P, P, i64, i32, i64, i32, i32, i64, P]
@@ -137,6 +139,29 @@ def dispatch(x: np.ndarray, w: np.ndarray, idx: np.ndarray, pos: np.ndarray,
     lib().orc_dispatch(_p(x), _p(w), _p(idx), _p(pos), T, K, H, E, S, cap,
                        _p(dx), _p(ms), _p(mw), _p(me))
     return Dispatched(dx, ms, mw, me)
+
+
+def dispatch_fp8(x8: np.ndarray, scales: np.ndarray, w: np.ndarray, idx: np.ndarray,
+                 pos: np.ndarray, E: int, S: int, cap: int) -> Dispatched:
+    """Dispatch of 8-bit tokens x8 [T, H] (raw bytes) with fp32 scales
+    [T, ns]: returns the receive rows as bytes [S, cap, 2H] (token bytes,
+    then the scales' bytes, then zeros) and the per-row metadata."""
+    x8 = _c(x8, np.uint8)
+    scales = _c(scales, np.float32)
+    w = _c(w, np.float32)
+    idx = _c(idx, np.int32)
+    pos = _c(pos, np.int32)
+    T, H = x8.shape
+    ns = scales.shape[1]
+    assert scales.shape[0] == T and 4 * ns <= H
+    K = idx.shape[1]
+    rows = np.zeros((S, cap, 2 * H), np.uint8)
+    ms = np.full((S, cap), -1, np.int32)
+    mw = np.zeros((S, cap), np.float32)
+    me = np.full((S, cap), -1, np.int32)
+    lib().orc_dispatch_fp8(_p(x8), _p(scales), ns, _p(w), _p(idx), _p(pos), T, K, H, E, S, cap,
+                           _p(rows), _p(ms), _p(mw), _p(me))
+    return Dispatched(rows, ms, mw, me)
 
 
 def swiglu_rows(X: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray,

@@ -195,6 +195,57 @@ def test_dispatch_closed_form(orc):
         assert np.all(d.meta_e[s, o:o + n] == e)
 
 
+def _fp8_case(seed, T, H, K, E, S, ns):
+    rng = np.random.default_rng(seed)
+    x8 = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    sc = rng.standard_normal((T, ns)).astype(np.float32)
+    idx = rng.integers(0, E, (T, K)).astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32)
+    return x8, sc, idx, w
+
+
+def test_dispatch_fp8_with_no_scales_is_the_bf16_dispatch_of_the_same_bytes(orc):
+    # H bytes per token read as H/2 bf16 values: the bf16 dispatch (pinned
+    # above) must place the same bytes in the same rows, with the same metadata
+    T, H, K, E, S = 50, 64, 3, 8, 4
+    x8, sc, idx, w = _fp8_case(1, T, H, K, E, S, 0)
+    cap = T * min(K, E // S)
+    p = orc.plan(idx, E, S, cap)
+    d8 = orc.dispatch_fp8(x8, sc, w, idx, p.pos, E, S, cap)
+    d16 = orc.dispatch(x8.view(np.uint16), w, idx, p.pos, E, S, cap)
+    np.testing.assert_array_equal(d8.disp_x[:, :, :H], d16.disp_x.view(np.uint8))
+    assert not d8.disp_x[:, :, H:].any()
+    for a, b in ((d8.meta_src, d16.meta_src), (d8.meta_w, d16.meta_w), (d8.meta_e, d16.meta_e)):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,H,K,E,S,ns", [(1, 16, 1, 1, 1, 4), (9, 32, 2, 4, 2, 1),
+                                          (23, 64, 3, 8, 4, 16), (40, 128, 4, 16, 8, 7)])
+def test_dispatch_fp8_brute_force(orc, T, H, K, E, S, ns):
+    x8, sc, idx, w = _fp8_case(T * 31 + ns, T, H, K, E, S, ns)
+    cap = T * min(K, E // S)
+    p = orc.plan(idx, E, S, cap)
+    d = orc.dispatch_fp8(x8, sc, w, idx, p.pos, E, S, cap)
+    eps = E // S
+    hits = np.zeros((S, cap), np.int32)
+    for t in range(T):
+        for j in range(K):
+            s, r = idx[t, j] // eps, p.pos[t, j]
+            row = d.disp_x[s, r]
+            assert bytes(row[:H]) == bytes(x8[t])
+            assert bytes(row[H:H + 4 * ns]) == sc[t].tobytes()
+            assert not row[H + 4 * ns:].any()
+            assert (d.meta_src[s, r], d.meta_e[s, r]) == (t * K + j, idx[t, j])
+            assert d.meta_w[s, r] == w[t, j]
+            hits[s, r] += 1
+    # every pair lands exactly once, in a row below its slot's total;
+    # nothing else is written
+    for s in range(S):
+        n = p.slot_total[s]
+        assert (hits[s, :n] == 1).all() and not hits[s, n:].any()
+        assert not d.disp_x[s, n:].any()
+
+
 # ---------------------------------------------------------------- expert ---
 
 def _f32(bits):
