@@ -76,7 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(
             "libcco_moe.so not found at %s; build it with "
-            "`python -m combine_symmetric_memory_amd.build` (hipcc, gfx950)" % path)
+            "`python combine_symmetric_memory_amd/build.py` (hipcc, gfx950)" % path)
     lib = ctypes.CDLL(path)
     for name, res, args in SIGNATURES:
         fn = getattr(lib, name)

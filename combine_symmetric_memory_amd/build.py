@@ -1,6 +1,6 @@
 """Compile the HIP sources under csrc/ into libcco_moe.so (gfx950 only).
 
-    python -m combine_symmetric_memory_amd.build
+    python combine_symmetric_memory_amd/build.py
 
 Objects go to <repo>/_build/, the shared library next to this file, where
 the Python binding loads it.  Every call recompiles.
