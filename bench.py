@@ -328,6 +328,45 @@ def main():
         stages[k] = st
     log("stages", json.dumps(stages))
 
+    # ---- the 8-bit dispatch (tokens quantized by the caller to OCP e4m3 in
+    # 1 x 128 blocks, fp32 scales) on the same routing, timed the same way;
+    # outside the step, which stays bf16 ----
+    variants = {}
+    if cfg.H % 128 == 0:
+        from synth.gen import quantized_activations
+        x8_np, sc_np = quantized_activations(cfg, block=128)
+        x8 = torch.from_numpy(x8_np).to(dev)
+        sc = torch.from_numpy(sc_np).to(dev)
+        ns = sc.shape[1]
+        del x8_np, sc_np
+        flush = torch.empty(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        moe.plan(idx, stream)
+        moe.dispatch_fp8(x8, sc, w, stream)
+        times = []
+        moe.set_timing(True)
+        for _ in range(n_iter):
+            flush.fill_(1.0)
+            moe.dispatch_fp8(x8, sc, w, stream)
+            torch.cuda.synchronize()
+            n, ms = moe.timing_summary()["dispatch_fp8"]
+            times.append(ms / n)
+        moe.set_timing(False)
+        # the bf16 rows back in the receive window for what follows
+        moe.dispatch(x, w, stream)
+        torch.cuda.synchronize()
+        del flush, x8, sc
+        t = np.asarray(times)
+        TK = cfg.T * cfg.K
+        nbytes = cfg.T * cfg.H + TK * cfg.H + 4 * ns * (cfg.T + TK) + 24 * TK
+        avg = float(t.mean())
+        variants["dispatch_fp8"] = {
+            "scales_per_token": ns, "launches": len(times), "avg_ms": round(avg, 5),
+            "median_ms": round(float(np.median(t)), 5), "alg_bytes": nbytes,
+            "GB_s": round(nbytes / (avg * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "vs_bf16_dispatch_time": round(avg / stages["dispatch"]["avg_ms"], 3)}
+        log("variants", json.dumps(variants))
+
     # roofline of the dominant kernel (the longest one), bound by HBM or by
     # the matrix cores according to its arithmetic intensity
     dom = max(stages, key=lambda k: stages[k]["avg_ms"])
@@ -422,6 +461,7 @@ def main():
         "summary": summary,
         "stages": stages,
         "roofline": roofline,
+        "variants": variants,
         "calibration": calibration,
         "cpu_baseline": cpu,
     }

@@ -19,9 +19,9 @@ CCO_ERR_HIP = -3
 CCO_ERR_CAPACITY = -4
 CCO_ERR_BAD_EXPERT = -5
 CCO_ERR_HEAP_FULL = -6
-CCO_NUM_KERNEL_KINDS = 7
+CCO_NUM_KERNEL_KINDS = 8
 KERNEL_KINDS = ("plan_count", "plan_rank", "dispatch", "expert_gate_up", "expert_down",
-                "combine", "combine_copy_in")
+                "combine", "combine_copy_in", "dispatch_fp8")
 
 
 class cco_moe_shape(ctypes.Structure):
@@ -61,6 +61,7 @@ SIGNATURES = [
     ("cco_moe_get_routing", ctypes.c_int, [P, ctypes.POINTER(cco_moe_routing)]),
     ("cco_moe_plan", ctypes.c_int, [P, P, I32, P]),
     ("cco_moe_dispatch", ctypes.c_int, [P, P, P, I32, P]),
+    ("cco_moe_dispatch_fp8", ctypes.c_int, [P, P, P, I32, P, I32, P]),
     ("cco_moe_expert", ctypes.c_int, [P, P, P, P]),
     ("cco_moe_dispatch_view", P, [P, I32]),
     ("cco_moe_combine_in_view", P, [P, I32]),

@@ -59,6 +59,7 @@ struct cco_moe {
   MoeArgs args{};
   int32_t max_plan_blocks = 0;
   int32_t planned_T = -1;  // T of the last plan (host-side order check)
+  bool disp_8bit = false;  // the last dispatch moved 8-bit tokens with scales
   int num_cus = 0;
   bool timing = false;
   std::vector<TimedPair> pending[CCO_NUM_KERNEL_KINDS];
@@ -389,15 +390,37 @@ int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights, int32_
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
+  m->disp_8bit = false;
   if (T == 0) return CCO_OK;
   MoeArgs a = m->args;
   return timed_launch(m, 2, st, [&] { return cco::launch_dispatch(a, x, weights, a.eid, T, st); });
+}
+
+int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int32_t ns,
+                         const float *weights, int32_t T, void *stream) {
+  if (!m || T < 0 || T != m->planned_T) return CCO_ERR_INVALID_ARG;
+  const int32_t H = m->shape.hidden;
+  if (H % 16 != 0 || ns < 0 || (int64_t)ns * 4 > H) return CCO_ERR_INVALID_ARG;
+  if (T > 0 && (!x8 || !weights || (ns > 0 && !scales))) return CCO_ERR_INVALID_ARG;
+  if (T > 0 && (((uintptr_t)x8 & 15) != 0 || (ns > 0 && ((uintptr_t)scales & 3) != 0)))
+    return CCO_ERR_INVALID_ARG;
+  DeviceGuard dg(m->heap->device);
+  if (!dg.ok) return CCO_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  m->disp_8bit = true;
+  if (T == 0) return CCO_OK;
+  MoeArgs a = m->args;
+  return timed_launch(m, 7, st, [&] {
+    return cco::launch_dispatch_fp8(a, x8, scales, ns, weights, a.eid, T, st);
+  });
 }
 
 int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *stream) {
   if (!m || m->planned_T < 0) return CCO_ERR_INVALID_ARG;
   if (m->shape.inter == 0) return CCO_OK;  // identity experts
   if (!w13 || !w2) return CCO_ERR_INVALID_ARG;
+  // the bf16 SwiGLU cannot read 8-bit receive rows
+  if (m->disp_8bit) return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
@@ -430,6 +453,13 @@ int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weig
   hipStream_t st = (hipStream_t)stream;
   if (T == 0) return CCO_OK;
   const uint64_t win = m->shape.inter > 0 ? m->lay.out_tok : m->lay.disp_x;
+  if (m->shape.inter == 0 && m->disp_8bit) {
+    // identity experts would hand combine the 8-bit receive rows as bf16
+    for (int s = 0; s < m->S; ++s) {
+      const void *src = expert_out ? expert_out[s] : nullptr;
+      if (!src || src == cco_moe_combine_in_view(m, s)) return CCO_ERR_INVALID_ARG;
+    }
+  }
   MoeArgs a = m->args;
   bool copied = false;
   if (expert_out) {

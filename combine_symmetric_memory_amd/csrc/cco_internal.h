@@ -70,6 +70,10 @@ hipError_t launch_plan_rank(const MoeArgs &a, const int32_t *idx, int32_t n_pair
                             int32_t nblk, hipStream_t st);
 hipError_t launch_dispatch(const MoeArgs &a, const uint16_t *x, const float *w,
                            const int32_t *idx, int32_t T, hipStream_t st);
+// Tokens of H bytes (8-bit, H % 16 == 0) with ns fp32 scales per token.
+hipError_t launch_dispatch_fp8(const MoeArgs &a, const uint8_t *x8, const float *scales,
+                               int32_t ns, const float *w, const int32_t *idx, int32_t T,
+                               hipStream_t st);
 hipError_t launch_combine(const MoeArgs &a, uint64_t src_win, const float *w,
                           const int32_t *idx, uint16_t *out, int32_t T, hipStream_t st);
 hipError_t launch_copy_in(const MoeArgs &a, int32_t slot, const uint16_t *src,

@@ -12,6 +12,12 @@
 // (up to 16 per lane in flight) and each vector is stored K times; 64 lanes
 // x 16 B make every store instruction one contiguous 1 KiB run.  Lanes 0..K-1 also write the
 // per-row metadata {t*K + j, w[t][j], e}.
+//
+// The same kernel moves tokens the caller has quantized to 8 bits (the
+// op's dispatch takes the tokens' scales beside them and hands back the
+// received scales, same section, step 1).  A receive row keeps its 2H bytes:
+// the token's H bytes go first and its ns fp32 scales right after them, so
+// an 8-bit row moves half the bytes of a bf16 one.
 #include "cco_internal.h"
 
 namespace cco {
@@ -25,15 +31,17 @@ struct RowMeta {
   int32_t e;
 };
 
-template <int KT>
+// Row bytes of the token go to the K receive rows of its pairs; with SCALED
+// the ns fp32 scales sc[0..ns) follow the token's nvec * 16 bytes.
+template <int KT, bool SCALED>
 __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__restrict__ xr,
+                                               int nvec, const float *__restrict__ sc, int ns,
                                                const float *__restrict__ w,
                                                const int32_t *__restrict__ idx, int t, int lane,
                                                int K) {
   constexpr int KM = KT > 0 ? KT : kMaxTopk;
   const int nk = KT > 0 ? KT : K;
   u32x4 *dst[KM];
-  const int nvec = a.H / 8;
   const uint64_t rb = (uint64_t)a.H * 2;
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
@@ -46,6 +54,9 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
         dst[j] = (u32x4 *)slot_addr(a, e / a.eps, a.off_disp_x, (uint64_t)p * rb);
     }
   }
+  // the first 64 scales are loaded with the row, one per lane
+  float s0 = 0.0f;
+  if (SCALED && lane < ns) s0 = sc[lane];
   // the row in chunks of up to kChunk vectors per lane (the whole row for
   // H <= 8192): all of a chunk's loads are in flight before its K stores
   constexpr int kChunk = 16;
@@ -67,6 +78,17 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
       }
     }
   }
+  if (SCALED) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < nk && dst[j] != nullptr && lane < ns) ((float *)(dst[j] + nvec))[lane] = s0;
+    for (int i = kWave + lane; i < ns; i += kWave) {
+      const float si = sc[i];
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j < nk && dst[j] != nullptr) ((float *)(dst[j] + nvec))[i] = si;
+    }
+  }
   if (lane < nk) {
     const int f = t * nk + lane;
     const int e = idx[f];
@@ -80,40 +102,58 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
   }
 }
 
-template <int KT>
+// x holds T rows of row_bytes (a multiple of 16); scales (SCALED only) T
+// rows of ns floats.
+template <int KT, bool SCALED>
 __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(
-    MoeArgs a, const u32x4 *__restrict__ x, const float *__restrict__ w,
-    const int32_t *__restrict__ idx, int32_t T) {
+    MoeArgs a, const u32x4 *__restrict__ x, int32_t row_bytes, const float *__restrict__ scales,
+    int32_t ns, const float *__restrict__ w, const int32_t *__restrict__ idx, int32_t T) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t = blockIdx.x * kDispatchWaves + wave;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
-  const u32x4 *xr = x + (int64_t)t * (a.H / 8);
-  dispatch_token<KT>(a, xr, w, idx, t, lane, a.K);
+  const int nvec = row_bytes / 16;
+  const u32x4 *xr = x + (int64_t)t * nvec;
+  const float *sc = SCALED ? scales + (int64_t)t * ns : nullptr;
+  dispatch_token<KT, SCALED>(a, xr, nvec, sc, ns, w, idx, t, lane, a.K);
 }
 
-template <int KT>
-hipError_t launch_k(const MoeArgs &a, const uint16_t *x, const float *w, const int32_t *idx,
-                    int32_t T, hipStream_t st) {
+template <int KT, bool SCALED>
+hipError_t launch_k(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
+                    int32_t ns, const float *w, const int32_t *idx, int32_t T, hipStream_t st) {
   const int nblk = (T + kDispatchWaves - 1) / kDispatchWaves;
-  hipLaunchKernelGGL(dispatch_kernel<KT>, dim3(nblk), dim3(kDispatchWaves * kWave), 0, st, a,
-                     (const u32x4 *)x, w, idx, T);
+  hipLaunchKernelGGL((dispatch_kernel<KT, SCALED>), dim3(nblk), dim3(kDispatchWaves * kWave), 0,
+                     st, a, (const u32x4 *)x, row_bytes, scales, ns, w, idx, T);
   return hipGetLastError();
+}
+
+template <bool SCALED>
+hipError_t launch_any_k(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
+                        int32_t ns, const float *w, const int32_t *idx, int32_t T,
+                        hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  switch (a.K) {
+    case 1: return launch_k<1, SCALED>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 2: return launch_k<2, SCALED>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 4: return launch_k<4, SCALED>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 6: return launch_k<6, SCALED>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 8: return launch_k<8, SCALED>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    default: return launch_k<0, SCALED>(a, x, row_bytes, scales, ns, w, idx, T, st);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_dispatch(const MoeArgs &a, const uint16_t *x, const float *w,
                            const int32_t *idx, int32_t T, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  switch (a.K) {
-    case 1: return launch_k<1>(a, x, w, idx, T, st);
-    case 2: return launch_k<2>(a, x, w, idx, T, st);
-    case 4: return launch_k<4>(a, x, w, idx, T, st);
-    case 6: return launch_k<6>(a, x, w, idx, T, st);
-    case 8: return launch_k<8>(a, x, w, idx, T, st);
-    default: return launch_k<0>(a, x, w, idx, T, st);
-  }
+  return launch_any_k<false>(a, x, a.H * 2, nullptr, 0, w, idx, T, st);
+}
+
+hipError_t launch_dispatch_fp8(const MoeArgs &a, const uint8_t *x8, const float *scales,
+                               int32_t ns, const float *w, const int32_t *idx, int32_t T,
+                               hipStream_t st) {
+  if (ns > 0) return launch_any_k<true>(a, x8, a.H, scales, ns, w, idx, T, st);
+  return launch_any_k<false>(a, x8, a.H, nullptr, 0, w, idx, T, st);
 }
 
 }  // namespace cco

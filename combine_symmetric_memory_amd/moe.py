@@ -8,6 +8,7 @@ stream unless one is given).  Method names follow the C entry points:
     moe = MoE(heap, max_tokens, hidden, topk, num_experts, inter)  # cco_moe_create
     moe.plan(idx)                                   # cco_moe_plan
     moe.dispatch(x, w)                              # cco_moe_dispatch
+    # (or moe.dispatch_fp8(x8, scales, w)           # cco_moe_dispatch_fp8)
     moe.expert(w13, w2)                             # cco_moe_expert
     out, code = moe.combine(w)                      # cco_moe_combine
     code, slot_total, counts = moe.status()         # cco_moe_status
@@ -196,6 +197,25 @@ class MoE:
         check(lib.cco_moe_dispatch(self.handle, _ptr(x, torch.bfloat16, "x"),
                                    _ptr(w, torch.float32, "w"), T, _stream(stream)),
               "cco_moe_dispatch")
+
+    def dispatch_fp8(self, x8: torch.Tensor, scales: torch.Tensor | None, w: torch.Tensor,
+                     stream=None) -> None:
+        """cco_moe_dispatch_fp8; x8 [T, H] of any 1-byte dtype (moved as raw
+        bytes), scales fp32 [T, ns] or None, w fp32 [T, K]."""
+        T = x8.shape[0]
+        if x8.dim() != 2 or x8.shape[1] != self.H or x8.element_size() != 1:
+            raise ValueError("x8 must be [T, H] of a 1-byte dtype")
+        if tuple(w.shape) != (T, self.K):
+            raise ValueError("w must be [T, K]")
+        ns = 0
+        if scales is not None:
+            if scales.dim() != 2 or scales.shape[0] != T:
+                raise ValueError("scales must be [T, ns]")
+            ns = scales.shape[1]
+        check(lib.cco_moe_dispatch_fp8(self.handle, _ptr(x8, None, "x8"),
+                                       _ptr(scales, torch.float32, "scales"), ns,
+                                       _ptr(w, torch.float32, "w"), T, _stream(stream)),
+              "cco_moe_dispatch_fp8")
 
     def expert(self, w13: torch.Tensor | None, w2: torch.Tensor | None, stream=None) -> None:
         """cco_moe_expert; w13 bf16 [E, 2I, H], w2 bf16 [E, H, I]."""

@@ -181,6 +181,27 @@ int cco_moe_plan(cco_moe *m, const int32_t *topk_idx, int32_t T, void *stream);
 int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights,
                      int32_t T, void *stream);
 
+/* Dispatch of tokens the caller has already quantized to 8 bits, with
+ * their scales ([blog] "Zero-copy MoE dispatch", step 1: the op's dispatch
+ * takes the tokens, their weights, their scales and the expert ids, and
+ * hands back received tokens, weights and scales).  The bytes move
+ * unchanged; no format is assumed for the 8-bit values or the scales.
+ *   x8       device, T rows of H bytes (H % 16 == 0), 16-byte aligned
+ *   scales   device fp32 [T][ns], 4-byte aligned; may be NULL when ns == 0
+ *   ns       scales per token, 0 <= 4 * ns <= H
+ *   weights  device fp32 [T][K], as for cco_moe_dispatch
+ * A receive row keeps its 2H bytes: DISP_X row bytes [0, H) = x8[t] and
+ * [H, H + 4 ns) = scales[t] as stored; the rest of the row is not written.
+ * DISP_META as for cco_moe_dispatch.  Needs the same T and idx as the
+ * preceding plan.  Moves half the token bytes of the bf16 dispatch.
+ * Until the next cco_moe_dispatch, the bf16 SwiGLU (cco_moe_expert) and a
+ * combine of identity experts through the receive window refuse to read
+ * these rows (CCO_ERR_INVALID_ARG): the caller's own expert reads
+ * cco_moe_dispatch_view and writes cco_moe_combine_in_view.
+ * Errors: CCO_ERR_INVALID_ARG for the checks above, before any launch. */
+int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int32_t ns,
+                         const float *weights, int32_t T, void *stream);
+
 /* Expert ([blog] "Zero-copy MoE dispatch", step 2: the expert reads the
  * receive window in place and writes the combine staging window, row i to
  * row i).  SwiGLU per expert e on its rows X of DISP_X:
@@ -231,9 +252,10 @@ int cco_moe_status(cco_moe *m, void *stream, int32_t *slot_total, int32_t *exper
  * each kernel launch of this object is bracketed by a pair of events; the
  * summary returns, per kernel kind, the number of timed launches and their
  * total milliseconds (kinds: 0 plan-count, 1 plan-rank, 2 dispatch,
- * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in).
+ * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in,
+ * 7 8-bit dispatch).
  * Reading the summary synchronises the recorded events and resets it. */
-#define CCO_NUM_KERNEL_KINDS 7
+#define CCO_NUM_KERNEL_KINDS 8
 int cco_moe_set_timing(cco_moe *m, int enable);
 int cco_moe_timing_summary(cco_moe *m, int32_t *launches, double *total_ms);
 

@@ -134,3 +134,20 @@ def expert_weights(cfg: MoEConfig, device: str | torch.device = "cpu",
         w2[n] = (b * cfg.weight_std).to(torch.bfloat16)
         del b
     return w13, w2
+
+
+def quantized_activations(cfg: MoEConfig, T: int | None = None, block: int = 128
+                          ) -> tuple[np.ndarray, np.ndarray]:
+    """Tokens as a caller would quantize them before an 8-bit dispatch:
+    x (as drawn by `activations`) in blocks of `block` values along H, each
+    block scaled by its absolute maximum / 448 and cast to OCP e4m3 by torch.
+    Returns (x8 uint8 [T, H] raw bytes, scales fp32 [T, H // block]).  The
+    dispatch moves these bytes without reading them, so only their shape
+    and realism matter here."""
+    x = activations(cfg, T).float()
+    T, H = x.shape
+    assert H % block == 0
+    xb = x.view(T, H // block, block)
+    sc = xb.abs().amax(dim=2).clamp_min(1e-12) / 448.0
+    q = (xb / sc.unsqueeze(2)).to(torch.float8_e4m3fn).view(T, H)
+    return q.view(torch.uint8).numpy().copy(), sc.numpy().astype(np.float32)

@@ -111,6 +111,7 @@ def test_invalid_calls_rejected_before_the_device(capi):
     assert L.cco_moe_create(None, None, None) == -1
     assert L.cco_moe_plan(None, None, 0, None) == -1
     assert L.cco_moe_dispatch(None, None, None, 0, None) == -1
+    assert L.cco_moe_dispatch_fp8(None, None, None, 0, None, 0, None) == -1
     assert L.cco_moe_expert(None, None, None, None) == -1
     assert L.cco_moe_combine(None, None, None, None, 0, None) == -1
     assert L.cco_moe_status(None, None, None, None) == -1
