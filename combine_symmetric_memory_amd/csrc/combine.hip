@@ -26,14 +26,17 @@ constexpr int kCombineWaves = 4;
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x0040u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 values -> packed bf16 (lo, hi), round to nearest even: gfx950's
+// v_cvt_pk_bf16_f32, which the compiler emits for a plain conversion.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-template <int KT>
+// NVL > 0: the row is exactly NVL vectors per lane (nvec == NVL * 64); for
+// K <= 8 the lane's vectors are then taken in groups of G, with fixed
+// address offsets and no bounds tests.
+template <int KT, int NVL>
 __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
     MoeArgs a, uint64_t src_win, const float *__restrict__ w, const int32_t *__restrict__ idx,
     u32x4 *__restrict__ out, int32_t T) {
@@ -81,12 +84,34 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
       }
     }
     u32x4 o;
-    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    o.x = pack_bf16_rne(acc[0], acc[1]);
+    o.y = pack_bf16_rne(acc[2], acc[3]);
+    o.z = pack_bf16_rne(acc[4], acc[5]);
+    o.w = pack_bf16_rne(acc[6], acc[7]);
     return o;
   };
+  if (NVL > 0 && KM <= 8) {
+    // G vectors per lane of each of the K rows in flight (7 x 8 loads for
+    // H = 7168, K = 8), then their sums
+    constexpr int G = NVL % 7 == 0 ? 7 : 4;
+    static_assert(NVL <= 0 || NVL % G == 0, "row length must be a whole number of groups");
+#pragma unroll
+    for (int g = 0; g < (NVL > 0 ? NVL / G : 0); ++g) {
+      // issued vector by vector across the K rows, so that the first sums
+      // wait only for the first loads
+      u32x4 r[G][KM];
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < nk && src[j] != nullptr)
+            r[c][j] = __builtin_nontemporal_load(src[j] + (g * G + c) * kWave + lane);
+      u32x4 *o = orow + g * G * kWave + lane;
+#pragma unroll
+      for (int c = 0; c < G; ++c) o[c * kWave] = accumulate(r[c]);
+    }
+    return;
+  }
   int v = lane;
   if (KM <= 8)
   for (; v + kWave < nvec; v += 2 * kWave) {
@@ -109,13 +134,25 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
   }
 }
 
+template <int KT, int NVL>
+hipError_t launch_nvl(const MoeArgs &a, uint64_t src_win, const float *w, const int32_t *idx,
+                      uint16_t *out, int32_t T, hipStream_t st) {
+  const int nblk = (T + kCombineWaves - 1) / kCombineWaves;
+  hipLaunchKernelGGL((combine_kernel<KT, NVL>), dim3(nblk), dim3(kCombineWaves * kWave), 0, st,
+                     a, src_win, w, idx, (u32x4 *)out, T);
+  return hipGetLastError();
+}
+
+// Fixed-length rows for the common widths: 14 and 8 vectors per lane
+// (H = 7168 and 4096); K above 8 keeps the general loop.
 template <int KT>
 hipError_t launch_k(const MoeArgs &a, uint64_t src_win, const float *w, const int32_t *idx,
                     uint16_t *out, int32_t T, hipStream_t st) {
-  const int nblk = (T + kCombineWaves - 1) / kCombineWaves;
-  hipLaunchKernelGGL(combine_kernel<KT>, dim3(nblk), dim3(kCombineWaves * kWave), 0, st, a,
-                     src_win, w, idx, (u32x4 *)out, T);
-  return hipGetLastError();
+  if (KT > 0 && KT <= 8 && a.H == 14 * 8 * kWave)
+    return launch_nvl<KT, 14>(a, src_win, w, idx, out, T, st);
+  if (KT > 0 && KT <= 8 && a.H == 8 * 8 * kWave)
+    return launch_nvl<KT, 8>(a, src_win, w, idx, out, T, st);
+  return launch_nvl<KT, 0>(a, src_win, w, idx, out, T, st);
 }
 
 // Copy slot_total[slot] rows of `src` into window dst_win of `slot`.

@@ -32,8 +32,10 @@ struct RowMeta {
 };
 
 // Row bytes of the token go to the K receive rows of its pairs; with SCALED
-// the ns fp32 scales sc[0..ns) follow the token's nvec * 16 bytes.
-template <int KT, bool SCALED>
+// the ns fp32 scales sc[0..ns) follow the token's nvec * 16 bytes.  NVL > 0:
+// the row is exactly NVL vectors per lane (nvec == NVL * 64), so the loads
+// and stores take no per-vector bounds test and fixed address offsets.
+template <int KT, bool SCALED, int NVL>
 __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__restrict__ xr,
                                                int nvec, const float *__restrict__ sc, int ns,
                                                const float *__restrict__ w,
@@ -57,10 +59,25 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
   // the first 64 scales are loaded with the row, one per lane
   float s0 = 0.0f;
   if (SCALED && lane < ns) s0 = sc[lane];
-  // the row in chunks of up to kChunk vectors per lane (the whole row for
-  // H <= 8192): all of a chunk's loads are in flight before its K stores
+  if (NVL > 0) {
+    // the whole row in flight before its K stores
+    u32x4 r[NVL > 0 ? NVL : 1];
+#pragma unroll
+    for (int c = 0; c < NVL; ++c) r[c] = xr[c * kWave + lane];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < nk && dst[j] != nullptr) {
+        u32x4 *d = dst[j] + lane;
+#pragma unroll
+        for (int c = 0; c < NVL; ++c) d[c * kWave] = r[c];
+      }
+    }
+  }
+  // otherwise the row in chunks of up to kChunk vectors per lane (the whole
+  // row for H <= 8192): all of a chunk's loads are in flight before its K
+  // stores
   constexpr int kChunk = 16;
-  for (int v0 = 0; v0 < nvec; v0 += kChunk * kWave) {
+  for (int v0 = 0; NVL == 0 && v0 < nvec; v0 += kChunk * kWave) {
     u32x4 r[kChunk];
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
@@ -104,7 +121,7 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
 
 // x holds T rows of row_bytes (a multiple of 16); scales (SCALED only) T
 // rows of ns floats.
-template <int KT, bool SCALED>
+template <int KT, bool SCALED, int NVL>
 __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(
     MoeArgs a, const u32x4 *__restrict__ x, int32_t row_bytes, const float *__restrict__ scales,
     int32_t ns, const float *__restrict__ w, const int32_t *__restrict__ idx, int32_t T) {
@@ -115,16 +132,32 @@ __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(
   const int nvec = row_bytes / 16;
   const u32x4 *xr = x + (int64_t)t * nvec;
   const float *sc = SCALED ? scales + (int64_t)t * ns : nullptr;
-  dispatch_token<KT, SCALED>(a, xr, nvec, sc, ns, w, idx, t, lane, a.K);
+  dispatch_token<KT, SCALED, NVL>(a, xr, nvec, sc, ns, w, idx, t, lane, a.K);
 }
 
+template <int KT, bool SCALED, int NVL>
+hipError_t launch_nvl(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
+                      int32_t ns, const float *w, const int32_t *idx, int32_t T,
+                      hipStream_t st) {
+  const int nblk = (T + kDispatchWaves - 1) / kDispatchWaves;
+  hipLaunchKernelGGL((dispatch_kernel<KT, SCALED, NVL>), dim3(nblk),
+                     dim3(kDispatchWaves * kWave), 0, st, a, (const u32x4 *)x, row_bytes, scales,
+                     ns, w, idx, T);
+  return hipGetLastError();
+}
+
+// Fixed-length rows for the common widths: 7 and 14 vectors per lane
+// (H = 7168 as 8-bit and bf16 rows), 8 and 16 (H = 4096 bf16, 8192 bf16).
 template <int KT, bool SCALED>
 hipError_t launch_k(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
                     int32_t ns, const float *w, const int32_t *idx, int32_t T, hipStream_t st) {
-  const int nblk = (T + kDispatchWaves - 1) / kDispatchWaves;
-  hipLaunchKernelGGL((dispatch_kernel<KT, SCALED>), dim3(nblk), dim3(kDispatchWaves * kWave), 0,
-                     st, a, (const u32x4 *)x, row_bytes, scales, ns, w, idx, T);
-  return hipGetLastError();
+  switch (row_bytes % (16 * kWave) == 0 ? row_bytes / (16 * kWave) : 0) {
+    case 7: return launch_nvl<KT, SCALED, 7>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 8: return launch_nvl<KT, SCALED, 8>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 14: return launch_nvl<KT, SCALED, 14>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    case 16: return launch_nvl<KT, SCALED, 16>(a, x, row_bytes, scales, ns, w, idx, T, st);
+    default: return launch_nvl<KT, SCALED, 0>(a, x, row_bytes, scales, ns, w, idx, T, st);
+  }
 }
 
 template <bool SCALED>

@@ -158,6 +158,9 @@ def test_generic_topk_and_limits(ccm, orc, K, E, S, T):
     (512, 1024, 4, 2, 1, 400),    # 128 x 512 remainder tiles cut into K-ranges
     (72, 0, 8, 2, 3, 50),         # identity: 9 vectors per row, most lanes idle
     (8200, 0, 4, 4, 2, 33),       # identity: rows longer than one dispatch chunk
+    (8192, 0, 4, 4, 2, 40),       # identity: fixed-length dispatch rows of 16 vectors per lane
+    (4096, 0, 16, 4, 8, 100),     # identity: fixed-length rows of 8 vectors per lane, top-8
+    (7168, 0, 16, 8, 6, 60),      # identity: fixed-length rows of 14 vectors per lane, top-6
 ])
 def test_shape_sweep(ccm, orc, H, I, E, S, K, T):
     cfg = get_config("tiny").with_(name="sweep", H=H, I=I, E=E, S=S, K=K, T=T)
