@@ -313,6 +313,7 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   a.E = E;
   a.S = m->S;
   a.eps = m->eps;
+  a.eps_magic = cco::eps_magic_of(m->eps);
   a.I = shape->inter;
   a.pos = p;               p += npairs;
   a.eid = p;               p += npairs;

@@ -47,7 +47,15 @@ struct MoeArgs {
   int32_t *gemm_queue; // [4][kNumXcd + 1] tile queues: the two expert GEMMs, then their split-tile tails; zero between launches
   float *split_ws;     // [gemm_workgroups][kSplitTileFloats] partial sums of split GEMM tiles
   int32_t *split_desc; // [gemm_workgroups / 2][kSplitDescInts] split tiles, zero between launches
+  uint32_t eps_magic;  // ceil(2^20 / eps): slot_of() without a division
 };
+
+// slot(e) = e / eps as (e * ceil(2^20 / eps)) >> 20, exact whenever
+// e * eps < 2^20, which e < E <= kMaxExperts = 1024 guarantees.
+__host__ __device__ inline int slot_of(const MoeArgs &a, int e) {
+  return (int)(((uint32_t)e * a.eps_magic) >> 20);
+}
+inline uint32_t eps_magic_of(int eps) { return ((1u << 20) + (uint32_t)eps - 1u) / (uint32_t)eps; }
 
 // The expert GEMMs run one workgroup per CU, in whole XCDs.
 inline int gemm_workgroups(int num_cus) { return ((num_cus + kNumXcd - 1) / kNumXcd) * kNumXcd; }

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
       const int p = a.pos[f];
       wj[j] = w[f];
       if ((unsigned)e < (unsigned)a.E && p >= 0 && (int64_t)p < a.cap)
-        src[j] = (const u32x4 *)slot_addr(a, e / a.eps, src_win, (uint64_t)p * rb);
+        src[j] = (const u32x4 *)slot_addr(a, slot_of(a, e), src_win, (uint64_t)p * rb);
     }
   }
   u32x4 *orow = out + (int64_t)t * nvec;

@@ -53,7 +53,7 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
       const int e = idx[f];
       const int p = a.pos[f];
       if ((unsigned)e < (unsigned)a.E && p >= 0 && (int64_t)p < a.cap)
-        dst[j] = (u32x4 *)slot_addr(a, e / a.eps, a.off_disp_x, (uint64_t)p * rb);
+        dst[j] = (u32x4 *)slot_addr(a, slot_of(a, e), a.off_disp_x, (uint64_t)p * rb);
     }
   }
   // the first 64 scales are loaded with the row, one per lane
@@ -111,7 +111,7 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
     const int e = idx[f];
     const int p = a.pos[f];
     if ((unsigned)e < (unsigned)a.E && p >= 0 && (int64_t)p < a.cap) {
-      RowMeta *m = (RowMeta *)slot_addr(a, e / a.eps, a.off_meta, (uint64_t)p * sizeof(RowMeta));
+      RowMeta *m = (RowMeta *)slot_addr(a, slot_of(a, e), a.off_meta, (uint64_t)p * sizeof(RowMeta));
       m->src = f;
       m->w = w[f];
       m->e = e;
@@ -147,11 +147,13 @@ hipError_t launch_nvl(const MoeArgs &a, const void *x, int32_t row_bytes, const 
 }
 
 // Fixed-length rows for the common widths: 7 and 14 vectors per lane
-// (H = 7168 as 8-bit and bf16 rows), 8 and 16 (H = 4096 bf16, 8192 bf16).
+// (H = 7168 as 8-bit and bf16 rows), 4, 8 and 16 (H = 4096 as 8-bit and
+// bf16 rows, H = 8192 bf16).
 template <int KT, bool SCALED>
 hipError_t launch_k(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
                     int32_t ns, const float *w, const int32_t *idx, int32_t T, hipStream_t st) {
   switch (row_bytes % (16 * kWave) == 0 ? row_bytes / (16 * kWave) : 0) {
+    case 4: return launch_nvl<KT, SCALED, 4>(a, x, row_bytes, scales, ns, w, idx, T, st);
     case 7: return launch_nvl<KT, SCALED, 7>(a, x, row_bytes, scales, ns, w, idx, T, st);
     case 8: return launch_nvl<KT, SCALED, 8>(a, x, row_bytes, scales, ns, w, idx, T, st);
     case 14: return launch_nvl<KT, SCALED, 14>(a, x, row_bytes, scales, ns, w, idx, T, st);

@@ -70,6 +70,8 @@ def _check_against_oracle(orc, moe, cfg, x8, sc, idx, w):
     ("tiny", {"H": 1024, "E": 12, "S": 4, "K": 3, "I": 0}, 4, 77),   # ns = 256: scales past 64 lanes
     ("tiny", {"H": 8208, "I": 0, "K": 2}, 16, 33),             # rows past one chunk; ns = 513
     ("tiny", {"H": 48, "E": 4, "S": 2, "K": 1, "I": 0}, 0, 50),    # no scales, 3 vectors per row
+    ("mixtral", {"I": 0}, 128, 200),                           # 4 vectors per lane, top-2
+    ("tiny", {"H": 8192, "E": 16, "S": 4, "K": 6, "I": 0}, 128, 40),  # 8 vectors per lane, top-6
 ])
 def test_dispatch_fp8_matches_oracle(ccm, orc, name, over, block, T):
     cfg = get_config(name, **over)
