@@ -71,6 +71,30 @@ __host__ __device__ inline char *slot_addr(const MoeArgs &a, int s, uint64_t win
   return a.base + (uint64_t)s * a.stride + win_off + off;
 }
 
+// Split of a token row (nvec 16-byte vectors) over `parts` wavefronts of
+// nvl vectors per lane, for the row kernels (dispatch, combine).  nvl is one
+// of the fixed lengths the kernels are built for (1, 2, 4, 7, 8, 14, 16), or
+// 0 for the general loop over the whole row (parts = 1).  Rows go one
+// wavefront each while T alone gives kRowWaves wavefronts; smaller batches
+// split each row into the fewest parts that reach that many, so that every
+// CU takes part.
+constexpr int kRowWaves = 4096;
+struct RowSplit {
+  int nvl, parts;
+};
+inline RowSplit row_split(int nvec, int64_t T) {
+  if (nvec <= 0 || nvec % kWave != 0) return {0, 1};
+  const int per_lane = nvec / kWave;
+  static const int kLens[] = {16, 14, 8, 7, 4, 2, 1};
+  RowSplit best{0, 1};
+  for (int nvl : kLens) {
+    if (per_lane % nvl != 0) continue;
+    best = {nvl, per_lane / nvl};
+    if (T * best.parts >= kRowWaves) break;
+  }
+  return best;
+}
+
 // Launchers, one per kernel file.  Each returns the hipError_t of its launch.
 hipError_t launch_plan_count(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
                              int32_t nblk, hipStream_t st);

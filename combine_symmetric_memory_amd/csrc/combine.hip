@@ -33,16 +33,18 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
-// NVL > 0: the row is exactly NVL vectors per lane (nvec == NVL * 64); for
-// K <= 8 the lane's vectors are then taken in groups of G, with fixed
-// address offsets and no bounds tests.
+// NVL > 0 (K <= 8 only): wavefront g sums part g % parts of token
+// g / parts, NVL vectors per lane (the row is a whole number of such parts),
+// in groups of G vectors with fixed address offsets and no bounds tests.
+// NVL == 0: one wavefront per token, the general loop over the row.
 template <int KT, int NVL>
 __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
     MoeArgs a, uint64_t src_win, const float *__restrict__ w, const int32_t *__restrict__ idx,
-    u32x4 *__restrict__ out, int32_t T) {
+    u32x4 *__restrict__ out, int32_t T, int32_t parts) {
   constexpr int KM = KT > 0 ? KT : kMaxTopk;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = blockIdx.x * kCombineWaves + wave;
+  const int gw = blockIdx.x * kCombineWaves + wave;
+  const int t = gw / parts, part = gw - t * parts;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
   const int nk = KT > 0 ? KT : a.K;
@@ -93,8 +95,9 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
   if (NVL > 0 && KM <= 8) {
     // G vectors per lane of each of the K rows in flight (7 x 8 loads for
     // H = 7168, K = 8), then their sums
-    constexpr int G = NVL % 7 == 0 ? 7 : 4;
+    constexpr int G = NVL % 7 == 0 ? 7 : (NVL < 4 ? NVL : 4);
     static_assert(NVL <= 0 || NVL % G == 0, "row length must be a whole number of groups");
+    const int v0 = part * NVL * kWave;
 #pragma unroll
     for (int g = 0; g < (NVL > 0 ? NVL / G : 0); ++g) {
       // issued vector by vector across the K rows, so that the first sums
@@ -105,8 +108,8 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
 #pragma unroll
         for (int j = 0; j < KM; ++j)
           if (j < nk && src[j] != nullptr)
-            r[c][j] = __builtin_nontemporal_load(src[j] + (g * G + c) * kWave + lane);
-      u32x4 *o = orow + g * G * kWave + lane;
+            r[c][j] = __builtin_nontemporal_load(src[j] + v0 + (g * G + c) * kWave + lane);
+      u32x4 *o = orow + v0 + g * G * kWave + lane;
 #pragma unroll
       for (int c = 0; c < G; ++c) o[c * kWave] = accumulate(r[c]);
     }
@@ -136,23 +139,30 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(
 
 template <int KT, int NVL>
 hipError_t launch_nvl(const MoeArgs &a, uint64_t src_win, const float *w, const int32_t *idx,
-                      uint16_t *out, int32_t T, hipStream_t st) {
-  const int nblk = (T + kCombineWaves - 1) / kCombineWaves;
+                      uint16_t *out, int32_t T, int32_t parts, hipStream_t st) {
+  const int64_t nwaves = (int64_t)T * parts;
+  const int nblk = (int)((nwaves + kCombineWaves - 1) / kCombineWaves);
   hipLaunchKernelGGL((combine_kernel<KT, NVL>), dim3(nblk), dim3(kCombineWaves * kWave), 0, st,
-                     a, src_win, w, idx, (u32x4 *)out, T);
+                     a, src_win, w, idx, (u32x4 *)out, T, parts);
   return hipGetLastError();
 }
 
-// Fixed-length rows for the common widths: 14 and 8 vectors per lane
-// (H = 7168 and 4096); K above 8 keeps the general loop.
+// Fixed-length row parts (row_split) for K <= 8; K above 8 keeps the general
+// loop.
 template <int KT>
 hipError_t launch_k(const MoeArgs &a, uint64_t src_win, const float *w, const int32_t *idx,
                     uint16_t *out, int32_t T, hipStream_t st) {
-  if (KT > 0 && KT <= 8 && a.H == 14 * 8 * kWave)
-    return launch_nvl<KT, 14>(a, src_win, w, idx, out, T, st);
-  if (KT > 0 && KT <= 8 && a.H == 8 * 8 * kWave)
-    return launch_nvl<KT, 8>(a, src_win, w, idx, out, T, st);
-  return launch_nvl<KT, 0>(a, src_win, w, idx, out, T, st);
+  const RowSplit rs = (KT > 0 && KT <= 8) ? row_split(a.H / 8, T) : RowSplit{0, 1};
+  switch (rs.nvl) {
+    case 1: return launch_nvl<KT, 1>(a, src_win, w, idx, out, T, rs.parts, st);
+    case 2: return launch_nvl<KT, 2>(a, src_win, w, idx, out, T, rs.parts, st);
+    case 4: return launch_nvl<KT, 4>(a, src_win, w, idx, out, T, rs.parts, st);
+    case 7: return launch_nvl<KT, 7>(a, src_win, w, idx, out, T, rs.parts, st);
+    case 8: return launch_nvl<KT, 8>(a, src_win, w, idx, out, T, rs.parts, st);
+    case 14: return launch_nvl<KT, 14>(a, src_win, w, idx, out, T, rs.parts, st);
+    case 16: return launch_nvl<KT, 16>(a, src_win, w, idx, out, T, rs.parts, st);
+    default: return launch_nvl<KT, 0>(a, src_win, w, idx, out, T, 1, st);
+  }
 }
 
 // Copy slot_total[slot] rows of `src` into window dst_win of `slot`.

@@ -33,14 +33,16 @@ struct RowMeta {
 
 // Row bytes of the token go to the K receive rows of its pairs; with SCALED
 // the ns fp32 scales sc[0..ns) follow the token's nvec * 16 bytes.  NVL > 0:
-// the row is exactly NVL vectors per lane (nvec == NVL * 64), so the loads
-// and stores take no per-vector bounds test and fixed address offsets.
+// this wavefront moves part `part` of the row, NVL vectors per lane (the
+// row is a whole number of such parts), with no per-vector bounds test and
+// fixed address offsets; part 0 also moves the scales and the metadata.
+// NVL == 0: the whole row (part 0).
 template <int KT, bool SCALED, int NVL>
 __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__restrict__ xr,
                                                int nvec, const float *__restrict__ sc, int ns,
                                                const float *__restrict__ w,
-                                               const int32_t *__restrict__ idx, int t, int lane,
-                                               int K) {
+                                               const int32_t *__restrict__ idx, int t, int part,
+                                               int lane, int K) {
   constexpr int KM = KT > 0 ? KT : kMaxTopk;
   const int nk = KT > 0 ? KT : K;
   u32x4 *dst[KM];
@@ -58,16 +60,17 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
   }
   // the first 64 scales are loaded with the row, one per lane
   float s0 = 0.0f;
-  if (SCALED && lane < ns) s0 = sc[lane];
+  if (SCALED && part == 0 && lane < ns) s0 = sc[lane];
   if (NVL > 0) {
-    // the whole row in flight before its K stores
+    // the whole part in flight before its K stores
+    const int v0 = part * NVL * kWave;
     u32x4 r[NVL > 0 ? NVL : 1];
 #pragma unroll
-    for (int c = 0; c < NVL; ++c) r[c] = xr[c * kWave + lane];
+    for (int c = 0; c < NVL; ++c) r[c] = xr[v0 + c * kWave + lane];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j < nk && dst[j] != nullptr) {
-        u32x4 *d = dst[j] + lane;
+        u32x4 *d = dst[j] + v0 + lane;
 #pragma unroll
         for (int c = 0; c < NVL; ++c) d[c * kWave] = r[c];
       }
@@ -95,7 +98,7 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
       }
     }
   }
-  if (SCALED) {
+  if (SCALED && part == 0) {
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (j < nk && dst[j] != nullptr && lane < ns) ((float *)(dst[j] + nvec))[lane] = s0;
@@ -106,7 +109,7 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
         if (j < nk && dst[j] != nullptr) ((float *)(dst[j] + nvec))[i] = si;
     }
   }
-  if (lane < nk) {
+  if (part == 0 && lane < nk) {
     const int f = t * nk + lane;
     const int e = idx[f];
     const int p = a.pos[f];
@@ -120,45 +123,48 @@ __device__ __forceinline__ void dispatch_token(const MoeArgs &a, const u32x4 *__
 }
 
 // x holds T rows of row_bytes (a multiple of 16); scales (SCALED only) T
-// rows of ns floats.
+// rows of ns floats.  Wavefront g moves part g % parts of token g / parts.
 template <int KT, bool SCALED, int NVL>
 __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(
     MoeArgs a, const u32x4 *__restrict__ x, int32_t row_bytes, const float *__restrict__ scales,
-    int32_t ns, const float *__restrict__ w, const int32_t *__restrict__ idx, int32_t T) {
+    int32_t ns, const float *__restrict__ w, const int32_t *__restrict__ idx, int32_t T,
+    int32_t parts) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t = blockIdx.x * kDispatchWaves + wave;
+  const int gw = blockIdx.x * kDispatchWaves + wave;
+  const int t = gw / parts, part = gw - t * parts;
   const int lane = threadIdx.x & (kWave - 1);
   if (t >= T) return;
   const int nvec = row_bytes / 16;
   const u32x4 *xr = x + (int64_t)t * nvec;
   const float *sc = SCALED ? scales + (int64_t)t * ns : nullptr;
-  dispatch_token<KT, SCALED, NVL>(a, xr, nvec, sc, ns, w, idx, t, lane, a.K);
+  dispatch_token<KT, SCALED, NVL>(a, xr, nvec, sc, ns, w, idx, t, part, lane, a.K);
 }
 
 template <int KT, bool SCALED, int NVL>
 hipError_t launch_nvl(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
-                      int32_t ns, const float *w, const int32_t *idx, int32_t T,
+                      int32_t ns, const float *w, const int32_t *idx, int32_t T, int32_t parts,
                       hipStream_t st) {
-  const int nblk = (T + kDispatchWaves - 1) / kDispatchWaves;
+  const int64_t nwaves = (int64_t)T * parts;
+  const int nblk = (int)((nwaves + kDispatchWaves - 1) / kDispatchWaves);
   hipLaunchKernelGGL((dispatch_kernel<KT, SCALED, NVL>), dim3(nblk),
                      dim3(kDispatchWaves * kWave), 0, st, a, (const u32x4 *)x, row_bytes, scales,
-                     ns, w, idx, T);
+                     ns, w, idx, T, parts);
   return hipGetLastError();
 }
 
-// Fixed-length rows for the common widths: 7 and 14 vectors per lane
-// (H = 7168 as 8-bit and bf16 rows), 4, 8 and 16 (H = 4096 as 8-bit and
-// bf16 rows, H = 8192 bf16).
 template <int KT, bool SCALED>
 hipError_t launch_k(const MoeArgs &a, const void *x, int32_t row_bytes, const float *scales,
                     int32_t ns, const float *w, const int32_t *idx, int32_t T, hipStream_t st) {
-  switch (row_bytes % (16 * kWave) == 0 ? row_bytes / (16 * kWave) : 0) {
-    case 4: return launch_nvl<KT, SCALED, 4>(a, x, row_bytes, scales, ns, w, idx, T, st);
-    case 7: return launch_nvl<KT, SCALED, 7>(a, x, row_bytes, scales, ns, w, idx, T, st);
-    case 8: return launch_nvl<KT, SCALED, 8>(a, x, row_bytes, scales, ns, w, idx, T, st);
-    case 14: return launch_nvl<KT, SCALED, 14>(a, x, row_bytes, scales, ns, w, idx, T, st);
-    case 16: return launch_nvl<KT, SCALED, 16>(a, x, row_bytes, scales, ns, w, idx, T, st);
-    default: return launch_nvl<KT, SCALED, 0>(a, x, row_bytes, scales, ns, w, idx, T, st);
+  const RowSplit rs = row_split(row_bytes / 16, T);
+  switch (rs.nvl) {
+    case 1: return launch_nvl<KT, SCALED, 1>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    case 2: return launch_nvl<KT, SCALED, 2>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    case 4: return launch_nvl<KT, SCALED, 4>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    case 7: return launch_nvl<KT, SCALED, 7>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    case 8: return launch_nvl<KT, SCALED, 8>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    case 14: return launch_nvl<KT, SCALED, 14>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    case 16: return launch_nvl<KT, SCALED, 16>(a, x, row_bytes, scales, ns, w, idx, T, rs.parts, st);
+    default: return launch_nvl<KT, SCALED, 0>(a, x, row_bytes, scales, ns, w, idx, T, 1, st);
   }
 }
 
