@@ -325,6 +325,10 @@ def main():
                 per.setdefault(k, []).append(ms / n)
     moe.set_timing(False)
     work = stage_work(cfg, active_experts=int(np.count_nonzero(counts)))
+    if "plan_count" in per and "plan_rank" not in per:
+        # a batch of one plan chunk runs the whole plan in one launch
+        per["plan"] = per.pop("plan_count")
+        work["plan"] = dict(bytes=work["plan_count"]["bytes"] + work["plan_rank"]["bytes"])
     stages = {}
     for k, times in per.items():
         t = np.asarray(times)

@@ -372,6 +372,15 @@ int cco_moe_plan(cco_moe *m, const int32_t *topk_idx, int32_t T, void *stream) {
   const int32_t n_pairs = T * m->shape.topk;
   const int32_t nblk = plan_blocks(n_pairs);
   MoeArgs a = m->args;
+  if (n_pairs > 0 && nblk == 1) {
+    // one chunk: count and rank in one launch
+    const int rc = timed_launch(m, 0, st, [&] {
+      return cco::launch_plan_single(a, topk_idx, n_pairs, st);
+    });
+    if (rc != CCO_OK) return rc;
+    m->planned_T = T;
+    return CCO_OK;
+  }
   int rc = timed_launch(m, 0, st, [&] { return cco::launch_plan_count(a, topk_idx, n_pairs, nblk, st); });
   if (rc != CCO_OK) return rc;
   if (n_pairs > 0) {

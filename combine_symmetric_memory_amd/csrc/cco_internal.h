@@ -100,6 +100,9 @@ hipError_t launch_plan_count(const MoeArgs &a, const int32_t *idx, int32_t n_pai
                              int32_t nblk, hipStream_t st);
 hipError_t launch_plan_rank(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
                             int32_t nblk, hipStream_t st);
+// Both plan steps in one workgroup, for n_pairs <= kPlanChunk.
+hipError_t launch_plan_single(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
+                              hipStream_t st);
 hipError_t launch_dispatch(const MoeArgs &a, const uint16_t *x, const float *w,
                            const int32_t *idx, int32_t T, hipStream_t st);
 // Tokens of H bytes (8-bit, H % 16 == 0) with ns fp32 scales per token.

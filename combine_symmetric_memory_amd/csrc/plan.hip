@@ -20,6 +20,10 @@
 //     a lane's rank among them is the popcount of the lower lanes of that
 //     mask (mbcnt).  Per-wave counts in LDS order the four wavefronts, and a
 //     running count per expert orders the 256-pair rounds.
+// A batch of one chunk (at most 2048 pairs, e.g. decode) runs both in one
+// workgroup of one launch, plan_single_kernel.
+#include <algorithm>
+
 #include "cco_internal.h"
 
 namespace cco {
@@ -66,9 +70,11 @@ __device__ int32_t block_exclusive_scan_1024(int32_t *v, int n, int32_t *wave_su
   return total;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(MoeArgs a,
-                                                                  const int32_t *__restrict__ idx,
-                                                                  int32_t n_pairs, int32_t nblk) {
+// Histogram of this workgroup's chunk; the workgroup that finishes last
+// (every one, with `single`: the batch is one chunk) turns the histograms
+// into counts, offsets, totals and the status word.
+__device__ __forceinline__ void plan_count_chunk(const MoeArgs &a, const int32_t *__restrict__ idx,
+                                                 int32_t n_pairs, int32_t nblk, bool single) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t wave_sums[kPlanWaves];
   __shared__ int32_t is_last;
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(MoeArgs a,
   // draws the last ticket sees every histogram
   __threadfence();
   __syncthreads();
-  if (tid == 0) is_last = (atomicAdd(a.ticket, 1) == nblk - 1);
+  if (tid == 0) is_last = single || (atomicAdd(a.ticket, 1) == nblk - 1);
   __syncthreads();
   if (!is_last) return;
   __threadfence();
@@ -145,9 +151,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(MoeArgs a,
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_rank_kernel(MoeArgs a,
-                                                                 const int32_t *__restrict__ idx,
-                                                                 int32_t n_pairs) {
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(MoeArgs a,
+                                                                  const int32_t *__restrict__ idx,
+                                                                  int32_t n_pairs, int32_t nblk) {
+  plan_count_chunk(a, idx, n_pairs, nblk, false);
+}
+
+// Stable positions of this workgroup's chunk (needs the counts and offsets).
+__device__ __forceinline__ void plan_rank_chunk(const MoeArgs &a, const int32_t *__restrict__ idx,
+                                                int32_t n_pairs) {
   extern __shared__ int32_t lds[];
   const int E = a.E;
   const int tid = threadIdx.x;
@@ -204,6 +216,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_rank_kernel(MoeArgs a,
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_rank_kernel(MoeArgs a,
+                                                                 const int32_t *__restrict__ idx,
+                                                                 int32_t n_pairs) {
+  plan_rank_chunk(a, idx, n_pairs);
+}
+
+// The whole plan of a one-chunk batch in one workgroup: the offsets the
+// count part writes are read back by the same workgroup after a barrier.
+__global__ __launch_bounds__(kPlanThreads) void plan_single_kernel(MoeArgs a,
+                                                                   const int32_t *__restrict__ idx,
+                                                                   int32_t n_pairs) {
+  plan_count_chunk(a, idx, n_pairs, 1, true);
+  __threadfence_block();
+  __syncthreads();
+  plan_rank_chunk(a, idx, n_pairs);
+}
+
 }  // namespace
 
 hipError_t launch_plan_count(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
@@ -219,6 +248,13 @@ hipError_t launch_plan_rank(const MoeArgs &a, const int32_t *idx, int32_t n_pair
   const size_t lds = (size_t)(kPlanWaves + 1) * a.E * sizeof(int32_t);
   hipLaunchKernelGGL(plan_rank_kernel, dim3(nblk), dim3(kPlanThreads), lds, st, a, idx,
                      n_pairs);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_single(const MoeArgs &a, const int32_t *idx, int32_t n_pairs,
+                              hipStream_t st) {
+  const size_t lds = std::max((size_t)(a.E + 1), (size_t)(kPlanWaves + 1) * a.E) * sizeof(int32_t);
+  hipLaunchKernelGGL(plan_single_kernel, dim3(1), dim3(kPlanThreads), lds, st, a, idx, n_pairs);
   return hipGetLastError();
 }
 

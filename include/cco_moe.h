@@ -251,7 +251,8 @@ int cco_moe_status(cco_moe *m, void *stream, int32_t *slot_total, int32_t *exper
 /* Per-kernel timing with HIP events on the launch stream.  While enabled,
  * each kernel launch of this object is bracketed by a pair of events; the
  * summary returns, per kernel kind, the number of timed launches and their
- * total milliseconds (kinds: 0 plan-count, 1 plan-rank, 2 dispatch,
+ * total milliseconds (kinds: 0 plan-count (the whole plan for a batch of
+ * at most 2048 (token, k) pairs, which runs in one launch), 1 plan-rank, 2 dispatch,
  * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in,
  * 7 8-bit dispatch).
  * Reading the summary synchronises the recorded events and resets it. */
