@@ -9,8 +9,9 @@
 //
 //   out[t][h] = bf16( fma(w[t][K-1], y_{K-1}[h], ... fma(w[t][0], y_0[h], 0)) )
 // in fp32, in j order, rounded once to nearest even.  One wavefront per
-// token; each lane owns 8 output elements per 16-byte vector and issues the
-// K row loads before it accumulates.  Every output element has one owner:
+// token (per part of its row when the batch is small, see row_split); each
+// lane owns 8 output elements per 16-byte vector and issues the K row loads
+// before it accumulates.  Every output element has one owner:
 // no atomics, the result does not depend on scheduling.
 //
 // copy_in_kernel serves the same section's note: an expert output that is

@@ -7,10 +7,11 @@
 // The receive address is slot arithmetic (section "What is MORI CCO?"):
 //   base + slot(e) * stride + DISP_X + pos[t][j] * (2 * H).
 //
-// One wavefront per token.  The token's K destinations are wave-uniform
-// (scalar loads of idx and pos), the row is read once in 16-byte vectors
-// (up to 16 per lane in flight) and each vector is stored K times; 64 lanes
-// x 16 B make every store instruction one contiguous 1 KiB run.  Lanes 0..K-1 also write the
+// One wavefront per token (per part of its row when the batch is small, see
+// row_split).  The token's K destinations are wave-uniform (scalar loads of
+// idx and pos), the row is read once in 16-byte vectors (up to 16 per lane
+// in flight) and each vector is stored K times; 64 lanes x 16 B make every
+// store instruction one contiguous 1 KiB run.  Lanes 0..K-1 also write the
 // per-row metadata {t*K + j, w[t][j], e}.
 //
 // The same kernel moves tokens the caller has quantized to 8 bits (the
