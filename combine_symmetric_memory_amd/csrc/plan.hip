@@ -113,14 +113,23 @@ __device__ __forceinline__ void plan_count_chunk(const MoeArgs &a, const int32_t
   if (!is_last) return;
   __threadfence();
 
-  // per expert: total over chunks, and each chunk's exclusive prefix
+  // per expert: total over chunks, and each chunk's exclusive prefix; the
+  // chunks' counts are loaded kBatch at a time, so the loads of a batch are
+  // in flight together rather than one after another
+  constexpr int kBatch = 16;
   for (int e = tid; e <= E; e += kPlanThreads) {
     int32_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int32_t *p = a.hist + (int64_t)b * (E + 1) + e;
-      const int32_t v = *p;
-      *p = run;
-      run += v;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int32_t v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = (b0 + i < nblk) ? a.hist[(int64_t)(b0 + i) * (E + 1) + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (b0 + i < nblk) {
+          a.hist[(int64_t)(b0 + i) * (E + 1) + e] = run;
+          run += v[i];
+        }
     }
     lh[e] = run;
   }
