@@ -374,6 +374,154 @@ def test_combine_weights_follow_columns(orc):
     np.testing.assert_array_equal(orc.combine_rows(rows, w), out)
 
 
+
+# ------------------------------------------- combine, exact fp32 fma chain ---
+#
+# The combine reading fixes fp32 accumulation with one fused multiply-add per
+# routed row, in column order j = 0..K-1, and one final rounding to bf16.  The
+# pins above only bound the result to a bf16 ulp of a float64 sum, which an
+# unfused product-then-add or a reversed column loop would also meet.  The
+# model below rebuilds the chain from its mathematical definition -- exact
+# rationals, each fma rounded once to the nearest binary32 (ties to even) --
+# and the oracle must match it bit for bit, on inputs built so that the
+# unfused and the reversed chains give different bf16 results.
+
+def _round_rational(q: Fraction, prec: int, emin: int = -126) -> Fraction:
+    """Nearest number with `prec` significant bits (binary32: 24, bf16: 8) and
+    the binary32 exponent range (subnormals below 2^emin), ties to an even
+    last significand bit.  Overflow is not modelled: inputs stay finite."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    quantum = Fraction(2) ** (max(e, emin) - (prec - 1))
+    n = a / quantum
+    lo = n.numerator // n.denominator
+    rest = n - lo
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * quantum
+
+
+def _bf16_of(q: Fraction) -> int:
+    """bf16 bit pattern of a rational that is exactly a bf16 value."""
+    f = np.float32(float(q))
+    assert Fraction(float(f)) == q
+    return int(np.array([f], np.float32).view(np.uint32)[0]) >> 16
+
+
+def _chain(w_row, y_rows, h, fused=True, reverse=False):
+    """bf16 bits of one output element: acc = 0; acc = fma(w_j, y_j[h], acc)
+    over j (fused: one rounding per step; unfused: the product is rounded
+    first), then one rounding to bf16."""
+    acc = Fraction(0)
+    order = range(len(w_row) - 1, -1, -1) if reverse else range(len(w_row))
+    for j in order:
+        prod = Fraction(float(w_row[j])) * Fraction(float(_f32(y_rows[j][h:h + 1])[0]))
+        if not fused:
+            prod = _round_rational(prod, 24)
+        acc = _round_rational(prod + acc, 24)
+    return _bf16_of(_round_rational(acc, 8))
+
+
+def _adversarial_combine_case(seed: int, nt: int, K: int, H: int):
+    """Rows and weights whose fp32 chains end on a binary32 rounding tie.
+
+    Column 0 puts the accumulator on a bf16 midpoint m (w0 = m, y0 = a power
+    of two per element).  One later column c adds the product w_c * y_c =
+    (1 + eps) * ulp32(m) / 2 with 0 < eps < 2^-24: a fused step keeps eps and
+    rounds m + ulp32/2 up, while a product rounded first loses it and the tie
+    goes to even (m, whose last binary32 bit is 0).  The final bf16 rounding
+    of m is itself a tie, so half of the elements end one bf16 ulp apart.
+    The other columns have zero weights, which leave a fused chain exact.
+    Reversed, the chain adds the rounded product to m last: the unfused
+    result again."""
+    rng = np.random.default_rng(seed)
+    y = np.zeros((nt, K, H), np.uint16)
+    w = np.zeros((nt, K), np.float32)
+    for q in range(nt):
+        while True:
+            ex = int(rng.integers(-20, 20))
+            mant = int(rng.integers(0x80, 0x100))
+            m = (mant + 0.5) * 2.0 ** (ex - 7)  # a bf16 midpoint, 9 significant bits
+            sgn = 1.0 if rng.random() < 0.5 else -1.0
+            ulp32 = 2.0 ** (np.floor(np.log2(m)) - 23)
+            yc = 1.0 + int(rng.integers(1, 128)) / 128.0  # bf16 with low bits
+            half = ulp32 / 2
+            wc = np.float32(half / yc)
+            if Fraction(float(wc)) * Fraction(yc) <= Fraction(half):
+                wc = np.nextafter(wc, np.float32(np.inf))
+            eps = Fraction(float(wc)) * Fraction(yc) / Fraction(half) - 1
+            if 0 < eps < Fraction(1, 2 ** 24):
+                break
+        c = int(rng.integers(1, K)) if K > 1 else 0
+        assert K > 1
+        w[q, 0] = np.float32(sgn * m)
+        w[q, c] = np.float32(sgn * float(wc))
+        for h in range(H):
+            k2 = int(rng.integers(-3, 4))
+            y[q, 0, h] = _torch_bf16_bits(np.array([2.0 ** k2], np.float32))[0]
+            y[q, c, h] = _torch_bf16_bits(np.array([yc * 2.0 ** k2], np.float32))[0]
+            for j in range(1, K):
+                if j != c:
+                    y[q, j, h] = _torch_bf16_bits(rng.standard_normal(1).astype(np.float32))[0]
+    return y, w
+
+
+def _random_combine_case(seed: int, nt: int, K: int, H: int):
+    rng = np.random.default_rng(seed)
+    y = _torch_bf16_bits(rng.standard_normal((nt, K, H)).astype(np.float32))
+    w = rng.random((nt, K)).astype(np.float32)
+    return y, w
+
+
+@pytest.mark.parametrize("kind,seed,nt,K,H", [("adversarial", 1, 96, 2, 4),
+                                              ("adversarial", 2, 96, 4, 4),
+                                              ("adversarial", 3, 96, 8, 4),
+                                              ("random", 4, 16, 8, 32),
+                                              ("random", 5, 12, 3, 40)])
+def test_combine_is_the_exact_fp32_fma_chain_in_column_order(orc, kind, seed, nt, K, H):
+    make = _adversarial_combine_case if kind == "adversarial" else _random_combine_case
+    y, w = make(seed, nt, K, H)
+    rows = [y[q, j] for q in range(nt) for j in range(K)]
+    got = orc.combine_rows(rows, w)
+    want = np.array([[_chain(w[q], y[q], h) for h in range(H)] for q in range(nt)], np.uint16)
+    np.testing.assert_array_equal(got, want)
+    # the same rows through the slot layout and the plan's positions
+    E, S = K, 1
+    idx = np.tile(np.arange(K, dtype=np.int32), (nt, 1))
+    p = orc.plan(idx, E, S, nt * K)
+    src = np.zeros((S, nt * K, H), np.uint16)
+    for q in range(nt):
+        for j in range(K):
+            src[0, p.pos[q, j]] = y[q, j]
+    np.testing.assert_array_equal(orc.combine_tokens(src, w, idx, p.pos, E, S), want)
+    if kind == "adversarial":
+        # the inputs tell the reading from its near neighbours: the unfused
+        # chain, and the fused chain in reverse column order (K > 1)
+        unfused = np.array([[_chain(w[q], y[q], h, fused=False) for h in range(H)]
+                            for q in range(nt)], np.uint16)
+        rev = np.array([[_chain(w[q], y[q], h, reverse=True) for h in range(H)]
+                        for q in range(nt)], np.uint16)
+        assert (unfused != want).sum() >= 10, "inputs do not separate fused from unfused"
+        assert (rev != want).sum() >= 10, "inputs do not separate the column orders"
+
+
+def test_round_rational_matches_binary32_and_bf16(orc):
+    # the model's rounding against numpy's binary32 and the oracle's bf16 on
+    # random doubles (a double -> binary32 conversion is itself one rounding)
+    rng = np.random.default_rng(9)
+    vals = rng.standard_normal(400) * 10.0 ** rng.integers(-30, 30, 400)
+    for d in vals:
+        q = Fraction(float(d))
+        assert _round_rational(q, 24) == Fraction(float(np.float32(d)))
+        assert _bf16_of(_round_rational(q, 8)) == orc.f64_to_bf16(float(d))
+
+
 # -------------------------------------------------------------- pipeline ---
 
 def test_tiny_pipeline_brute_force(orc):
