@@ -30,6 +30,10 @@ constexpr unsigned char kGuardByte = 0xA5;
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+// The kernels read and write rows in 16-byte vectors and routing data in
+// 4-byte words.
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 struct DeviceGuard {
   int prev = -1;
   bool ok = false;
@@ -137,17 +141,22 @@ int32_t plan_blocks(int64_t n_pairs) {
 // Launch `fn` (returning hipError_t), bracketed by timing events if enabled.
 template <class F>
 int timed_launch(cco_moe *m, int kind, hipStream_t st, F &&fn) {
-  TimedPair tp{};
-  if (m->timing) {
-    if (hipEventCreate(&tp.start) != hipSuccess || hipEventCreate(&tp.stop) != hipSuccess)
-      return CCO_ERR_HIP;
-    if (hipEventRecord(tp.start, st) != hipSuccess) return CCO_ERR_HIP;
+  if (!m->timing) return fn() == hipSuccess ? CCO_OK : CCO_ERR_HIP;
+  TimedPair tp{nullptr, nullptr};
+  auto drop = [&tp] {
+    if (tp.start) (void)hipEventDestroy(tp.start);
+    if (tp.stop) (void)hipEventDestroy(tp.stop);
+  };
+  if (hipEventCreate(&tp.start) != hipSuccess || hipEventCreate(&tp.stop) != hipSuccess ||
+      hipEventRecord(tp.start, st) != hipSuccess) {
+    drop();
+    return CCO_ERR_HIP;
   }
-  if (fn() != hipSuccess) return CCO_ERR_HIP;
-  if (m->timing) {
-    if (hipEventRecord(tp.stop, st) != hipSuccess) return CCO_ERR_HIP;
-    m->pending[kind].push_back(tp);
+  if (fn() != hipSuccess || hipEventRecord(tp.stop, st) != hipSuccess) {
+    drop();
+    return CCO_ERR_HIP;
   }
+  m->pending[kind].push_back(tp);
   return CCO_OK;
 }
 
@@ -365,7 +374,8 @@ int cco_moe_get_routing(const cco_moe *m, cco_moe_routing *out) {
 }
 
 int cco_moe_plan(cco_moe *m, const int32_t *topk_idx, int32_t T, void *stream) {
-  if (!m || T < 0 || T > m->shape.max_tokens || (T > 0 && !topk_idx)) return CCO_ERR_INVALID_ARG;
+  if (!m || T < 0 || T > m->shape.max_tokens || (T > 0 && (!topk_idx || !aligned(topk_idx, 4))))
+    return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
@@ -397,6 +407,7 @@ int cco_moe_plan(cco_moe *m, const int32_t *topk_idx, int32_t T, void *stream) {
 
 int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights, int32_t T, void *stream) {
   if (!m || T < 0 || T != m->planned_T || (T > 0 && (!x || !weights))) return CCO_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned(x, 16) || !aligned(weights, 4))) return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
@@ -412,7 +423,7 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
   const int32_t H = m->shape.hidden;
   if (H % 16 != 0 || ns < 0 || (int64_t)ns * 4 > H) return CCO_ERR_INVALID_ARG;
   if (T > 0 && (!x8 || !weights || (ns > 0 && !scales))) return CCO_ERR_INVALID_ARG;
-  if (T > 0 && (((uintptr_t)x8 & 15) != 0 || (ns > 0 && ((uintptr_t)scales & 3) != 0)))
+  if (T > 0 && (!aligned(x8, 16) || !aligned(weights, 4) || (ns > 0 && !aligned(scales, 4))))
     return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
@@ -428,7 +439,7 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
 int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *stream) {
   if (!m || m->planned_T < 0) return CCO_ERR_INVALID_ARG;
   if (m->shape.inter == 0) return CCO_OK;  // identity experts
-  if (!w13 || !w2) return CCO_ERR_INVALID_ARG;
+  if (!w13 || !w2 || !aligned(w13, 16) || !aligned(w2, 16)) return CCO_ERR_INVALID_ARG;
   // the bf16 SwiGLU cannot read 8-bit receive rows
   if (m->disp_8bit) return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);
@@ -458,6 +469,10 @@ void *cco_moe_combine_in_view(cco_moe *m, int32_t slot) {
 int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weights, uint16_t *out,
                     int32_t T, void *stream) {
   if (!m || T < 0 || T != m->planned_T || (T > 0 && (!weights || !out))) return CCO_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned(out, 16) || !aligned(weights, 4))) return CCO_ERR_INVALID_ARG;
+  if (expert_out)
+    for (int s = 0; s < m->S; ++s)
+      if (expert_out[s] && !aligned(expert_out[s], 16)) return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;

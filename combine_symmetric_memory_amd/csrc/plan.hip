@@ -19,7 +19,9 @@
 //     found with one ballot per id bit (wave64 has no match instruction);
 //     a lane's rank among them is the popcount of the lower lanes of that
 //     mask (mbcnt).  Per-wave counts in LDS order the four wavefronts, and a
-//     running count per expert orders the 256-pair rounds.
+//     running count per expert orders the 256-pair rounds.  A pair whose row
+//     would fall at or past the slot's capacity gets pos -1 (dropped; the
+//     status word reports the overflow).
 // A batch of one chunk (at most 2048 pairs, e.g. decode) runs both in one
 // workgroup of one launch, plan_single_kernel.
 #include <algorithm>
@@ -213,6 +215,7 @@ __device__ __forceinline__ void plan_rank_chunk(const MoeArgs &a, const int32_t 
       if (e < E) {
         p = run[e] + rank;
         for (int w = 0; w < wave; ++w) p += wcnt[w * E + e];
+        if ((int64_t)p >= a.cap) p = -1;  // past the slot's capacity: dropped
       }
       a.pos[f] = p;
       a.eid[f] = (e < E) ? e : -1;

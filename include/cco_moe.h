@@ -89,7 +89,9 @@ typedef struct {
 /* Device pointers of the routing state that plan writes (owned by the
  * cco_moe; valid until the heap is destroyed). */
 typedef struct {
-  int32_t *pos;        /* [max_tokens][K]: row inside slot(idx[t][j]), -1 if dropped */
+  int32_t *pos;        /* [max_tokens][K]: row inside slot(idx[t][j]); -1 for a
+                        * pair whose row would fall at or past the slot's
+                        * capacity (dropped) or whose id is invalid */
   int32_t *counts;     /* [E]: rows routed to each expert */
   int32_t *expert_off; /* [E]: first row of each expert inside its slot */
   int32_t *slot_total; /* [S]: rows received by each slot (the receive count) */
@@ -161,23 +163,27 @@ int cco_moe_get_routing(const cco_moe *m, cco_moe_routing *out);
 
 /* Plan ([blog] "Zero-copy MoE dispatch": dispatch returns the receive count
  * and a routing object that combine reuses).
- *   topk_idx  device int32 [T][K], expert ids, row-major, caller-owned
+ *   topk_idx  device int32 [T][K], expert ids, row-major, caller-owned,
+ *             4-byte aligned
  *   T         0 <= T <= max_tokens (T == 0 is a no-op that zeroes the counts)
  * Computes per-expert counts, slot-local expert offsets, per-slot totals and
  * pos[t][j] = expert_off[e] + number of earlier pairs (flat order t*K+j)
- * with the same expert e.  Device errors: CCO_ERR_BAD_EXPERT,
- * CCO_ERR_CAPACITY (reported by cco_moe_status). */
+ * with the same expert e, or -1 when that row is at or past the slot's
+ * capacity (the pair is dropped: dispatch, expert and combine skip it).
+ * Device errors: CCO_ERR_BAD_EXPERT, CCO_ERR_CAPACITY (reported by
+ * cco_moe_status). */
 int cco_moe_plan(cco_moe *m, const int32_t *topk_idx, int32_t T, void *stream);
 
 /* Dispatch ([blog] "Zero-copy MoE dispatch", step 1: each token row is
  * written straight into the receive window of the slot that owns each of
  * its experts; no staging copy).
- *   x        device bf16 [T][H]
- *   weights  device fp32 [T][K] routing weights (carried into the per-row
- *            metadata; applied by combine)
+ *   x        device bf16 [T][H], 16-byte aligned
+ *   weights  device fp32 [T][K] routing weights, 4-byte aligned (carried
+ *            into the per-row metadata; applied by combine)
  * For every pair: DISP_X[slot(e)][pos] = x[t] bit for bit and
  * DISP_META[slot(e)][pos] = {t*K + j, w[t][j], e}.  Needs the same T and
- * idx as the preceding plan. */
+ * idx as the preceding plan.  Errors: CCO_ERR_INVALID_ARG (T differs from
+ * the plan's, NULL or misaligned pointers), before any launch. */
 int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights,
                      int32_t T, void *stream);
 
@@ -207,8 +213,9 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
  * row i).  SwiGLU per expert e on its rows X of DISP_X:
  *   h = bf16( silu(X Wg^T) * (X Wu^T) )  -> HBUF  (fp32 accumulation)
  *   y = bf16( h Wd^T )                   -> OUT_TOK
- *   w13  device bf16 [E][2I][H]: rows 0..I-1 gate, rows I..2I-1 up
- *   w2   device bf16 [E][H][I]
+ *   w13  device bf16 [E][2I][H]: rows 0..I-1 gate, rows I..2I-1 up;
+ *        16-byte aligned
+ *   w2   device bf16 [E][H][I], 16-byte aligned
  * (both K-contiguous, like nn.Linear.weight).  Row counts are read on the
  * device; nothing is copied to the host.  Results are deterministic for a
  * given routing on a given device: in GEMMs of few tile rounds the last
@@ -216,9 +223,14 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
  * inter == 0 this is a no-op (identity experts; w13 and w2 may be NULL). */
 int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *stream);
 
-/* Receive window (recv_x) of `slot`: DISP_X base, [cap][H] bf16; rows
- * [expert_off[e], expert_off[e] + counts[e]) belong to expert e.  NULL if
- * slot is out of range. */
+/* Receive window of `slot` ([blog] "Zero-copy MoE dispatch -> expert ->
+ * combine", step 1: the received tokens the op's dispatch returns are not a
+ * new tensor but a view of the "disp_out" region of symmetric memory, which
+ * the dispatching peers wrote directly): DISP_X base, [cap][H] bf16; rows
+ * [expert_off[e], expert_off[e] + counts[e]) belong to expert e, and the
+ * first slot_total[slot] rows are the ones received.  Borrowed: valid until
+ * the heap is destroyed, overwritten by the next dispatch.  NULL if slot is
+ * out of range or m is NULL. */
 void *cco_moe_dispatch_view(cco_moe *m, int32_t slot);
 
 /* Combine staging window of `slot` ([blog] "Zero-copy MoE dispatch":
@@ -235,17 +247,28 @@ void *cco_moe_combine_in_view(cco_moe *m, int32_t slot);
  *               copy of its rows) and the call returns CCO_INFO_COPIED
  *               ([blog] "Zero-copy MoE dispatch", note on the data_ptr
  *               match).
- *   weights     device fp32 [T][K]
- *   out         device bf16 [T][H], caller-owned
+ *   weights     device fp32 [T][K], 4-byte aligned
+ *   out         device bf16 [T][H], caller-owned, 16-byte aligned; a
+ *               foreign expert output must be 16-byte aligned too
  *   out[t] = bf16( sum_j w[t][j] * y[slot(e)][pos[t][j]] ), fp32 fused
- *   multiply-add in j = 0..K-1 order, rounded once to nearest even. */
+ *   multiply-add in j = 0..K-1 order, rounded once to nearest even; dropped
+ *   pairs (pos -1) contribute nothing.
+ * Errors: CCO_ERR_INVALID_ARG (T differs from the plan's, NULL or
+ * misaligned pointers), before any launch. */
 int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weights,
                     uint16_t *out, int32_t T, void *stream);
 
-/* Synchronise `stream`, copy the receive counts to the host (either pointer
- * may be NULL; slot_total is [S], expert_counts is [E]) and return the
- * device status word (CCO_OK, CCO_ERR_BAD_EXPERT or CCO_ERR_CAPACITY), or
- * CCO_ERR_HIP. */
+/* Receive counts and device status, read on the host ([blog] "Zero-copy
+ * MoE dispatch -> expert -> combine", step 1: after dispatch the host
+ * synchronises and reads the device-side receive count, total_recv, to
+ * slice the received tokens).  The path itself never needs this call: the
+ * expert and combine kernels read the counts on the device.
+ *   stream         the stream the path runs on; synchronised first
+ *   slot_total     host int32 [S] or NULL: rows received by each slot
+ *   expert_counts  host int32 [E] or NULL: rows routed to each expert
+ * Returns the device status word of the last plan (CCO_OK,
+ * CCO_ERR_BAD_EXPERT or CCO_ERR_CAPACITY), CCO_ERR_INVALID_ARG for a NULL
+ * m, or CCO_ERR_HIP. */
 int cco_moe_status(cco_moe *m, void *stream, int32_t *slot_total, int32_t *expert_counts);
 
 /* Per-kernel timing with HIP events on the launch stream.  While enabled,

@@ -97,7 +97,9 @@ uint16_t orc_f64_to_bf16(double d) {
  * counts[E]   rows routed to each expert
  * expert_off[E]  first row of expert e inside its slot (slot-local)
  * slot_total[S]  rows received by each slot (the per-rank receive count)
- * pos[T][K]   row inside slot(idx[t][j]) that receives the pair (t, j)
+ * pos[T][K]   row inside slot(idx[t][j]) that receives the pair (t, j), or
+ *             -1 when that row would be at or past cap (the pair is dropped:
+ *             a slot holds cap rows, and the status says it overflowed)
  *
  * Returns ORC_BAD_EXPERT if an id is outside [0, E) (outputs then undefined),
  * ORC_CAPACITY if a slot would receive more than cap rows.
@@ -137,6 +139,7 @@ int orc_plan(const int32_t *idx, int64_t T, int32_t K, int32_t E, int32_t S,
       e = idx[f];
       pos[f] = expert_off[e] + next[e];
       next[e] += 1;
+      if ((int64_t)pos[f] >= cap) pos[f] = -1; /* past the slot: dropped */
     }
     free(next);
   }
@@ -154,6 +157,7 @@ int orc_plan(const int32_t *idx, int64_t T, int32_t K, int32_t E, int32_t S,
  *
  * disp_x is [S][cap][H] bf16: disp_x[slot(e)][pos[t][j]] = x[t], bit for bit.
  * meta_* are [S][cap]: source pair t*K+j, its routing weight, its expert id.
+ * Dropped pairs (pos -1) move nothing.
  */
 void orc_dispatch(const uint16_t *x, const float *w, const int32_t *idx,
                   const int32_t *pos, int64_t T, int32_t K, int64_t H,
@@ -166,6 +170,7 @@ void orc_dispatch(const uint16_t *x, const float *w, const int32_t *idx,
     for (j = 0; j < K; ++j) {
       int64_t f = t * K + j;
       int32_t e = idx[f];
+      if (pos[f] < 0) continue;
       int64_t row = (int64_t)(e / eps) * cap + pos[f];
       memcpy(disp_x + row * H, x + t * H, (size_t)H * sizeof(uint16_t));
       meta_src[row] = (int32_t)f;
@@ -197,6 +202,7 @@ void orc_dispatch_fp8(const uint8_t *x, const float *scales, int32_t ns, const f
     for (j = 0; j < K; ++j) {
       int64_t f = t * K + j;
       int32_t e = idx[f];
+      if (pos[f] < 0) continue;
       int64_t row = (int64_t)(e / eps) * cap + pos[f];
       uint8_t *r = rows + row * 2 * H;
       memcpy(r, x + t * H, (size_t)H);
@@ -299,6 +305,7 @@ void orc_swiglu_rows(const uint16_t *X, int64_t n, int64_t H, int64_t I,
  * when the experts are the identity).  tokens[nt] lists the tokens to
  * produce; out is [nt][H] bf16.
  *   acc = 0; for j in 0..K-1: acc = fmaf(w[t][j], y_j[h], acc); out = bf16(acc)
+ * A dropped pair (pos -1) contributes nothing.
  */
 void orc_combine_tokens(const uint16_t *src, const float *w, const int32_t *idx,
                         const int32_t *pos, const int64_t *tokens, int64_t nt,
@@ -313,6 +320,7 @@ void orc_combine_tokens(const uint16_t *src, const float *w, const int32_t *idx,
       float acc = 0.0f;
       for (j = 0; j < K; ++j) {
         int64_t f = t * K + j;
+        if (pos[f] < 0) continue;
         int64_t row = (int64_t)(idx[f] / eps) * cap + pos[f];
         acc = fmaf(w[f], orc_bf16_to_f32(src[row * H + h]), acc);
       }

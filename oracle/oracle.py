@@ -185,12 +185,13 @@ def expert_all(disp_x: np.ndarray, counts: np.ndarray, expert_off: np.ndarray,
     """Run every expert on its rows of the receive region; returns the
     combine staging region [S, cap, H] (rows past slot_total stay 0)."""
     eps = E // S
+    cap = disp_x.shape[1]
     out = np.zeros_like(disp_x)
     for e in range(E):
-        n = int(counts[e])
-        if n == 0:
-            continue
         s, o = e // eps, int(expert_off[e])
+        n = min(int(counts[e]), cap - o)  # rows past the slot were dropped
+        if n <= 0:
+            continue
         out[s, o:o + n] = swiglu_rows(disp_x[s, o:o + n], w13[e], w2[e], nthreads)
     return out
 
@@ -243,11 +244,14 @@ class PipelineResult:
     out: np.ndarray             # [T, H]
 
 
-def pipeline(x, w, idx, E, S, cap, w13=None, w2=None, nthreads=None) -> PipelineResult:
+def pipeline(x, w, idx, E, S, cap, w13=None, w2=None, nthreads=None,
+             allow_overflow=False) -> PipelineResult:
     """The whole path on the CPU: plan, dispatch, expert (SwiGLU, or the
-    identity when no weights are given), combine."""
+    identity when no weights are given), combine.  With allow_overflow a
+    slot overflow is not an error: the pairs past a slot's capacity are
+    dropped (pos -1) and the rest of the path runs without them."""
     pl = plan(idx, E, S, cap)
-    if pl.status != OK:
+    if pl.status != OK and not (allow_overflow and pl.status == CAPACITY):
         raise ValueError("oracle plan failed with status %d" % pl.status)
     d = dispatch(x, w, idx, pl.pos, E, S, cap)
     if w13 is None:

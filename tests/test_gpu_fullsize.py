@@ -1,9 +1,12 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times.  Plan and dispatch are compared with the oracle in full
-(bit-exact); the expert on every row of a stratified set of experts; combine
-on sampled tokens (bit-exact on the GPU's own expert rows) and end to end on
-sampled tokens from x (within tolerance)."""
+(bit-exact); the expert on the first and last row of every expert that has
+rows (every m-tile kind: full, partial, the 128-row remainder tiles), and on
+one row of every 256-row m-tile where the GEMM splits its last tiles; combine
+on every token (bit-exact on the GPU's own expert rows, read slot by slot) and
+end to end on sampled tokens from x (within tolerance)."""
 import gc
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -87,6 +90,49 @@ def _combine_tokens_parity(orc, moe, c, ref, out, tokens, identity):
     return got
 
 
+def _combine_all_tokens_exact(orc, moe, c, ref, out):
+    """Combine of every token, bit-exact against the oracle's combine of the
+    GPU's own expert rows; the staging rows are read slot by slot into a
+    [S][max slot total][H] array (the oracle addresses rows as slot * rows +
+    pos, so any per-slot row count at least the slot totals serves)."""
+    cfg = c.cfg
+    n = int(ref.slot_total.max())
+    src = np.zeros((cfg.S, n, cfg.H), np.uint16)
+    for s in range(cfg.S):
+        src[s, :ref.slot_total[s]] = moe.read_rows("out_tok", s, 0, int(ref.slot_total[s]))
+    want = orc.combine_tokens(src, c.w_np, c.idx_np, ref.pos, cfg.E, cfg.S)
+    got = bf16_bits(out)
+    np.testing.assert_array_equal(got, want)
+    say("  combine: all %d tokens bit-exact" % cfg.T)
+    return got
+
+
+def _rows_parity(orc, moe, c, ref, picks, label):
+    """picks: {expert: [row offsets inside the expert]}; each expert's rows
+    through the oracle's SwiGLU, experts in parallel (the oracle releases the
+    interpreter lock)."""
+    cfg = c.cfg
+
+    def one(e):
+        s, o = e // cfg.eps, int(ref.expert_off[e])
+        rows = sorted(set(picks[e]))
+        X = np.stack([moe.read_rows("disp_x", s, o + r, 1)[0] for r in rows])
+        Y = np.stack([moe.read_rows("out_tok", s, o + r, 1)[0] for r in rows])
+        w13e, w2e = weights_host(c, e)
+        return e, Y, orc.swiglu_rows(X, w13e, w2e, nthreads=2)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(one, sorted(picks)))
+    Y = np.concatenate([r[1] for r in res])
+    R = np.concatenate([r[2] for r in res])
+    say("  %s: %d experts, %d rows" % (label, len(res), len(Y)))
+    assert_close(Y, R, label)
+
+
+def _first_last_rows(counts):
+    return {int(e): [0, int(counts[e]) - 1] for e in np.nonzero(counts)[0]}
+
+
 def _end_to_end_tokens(orc, c, tokens, got):
     """Oracle from x for the sampled tokens: each chosen expert's SwiGLU on
     x[t] (the expert rows of a token do not depend on other tokens)."""
@@ -111,10 +157,11 @@ def test_dsv3_full(orc):
     assert code == 0
     ref = _plan_and_dispatch_exact(orc, moe, c)
     _expert_rows_parity(orc, moe, c, ref, _sample_experts(ref.counts))
+    _rows_parity(orc, moe, c, ref, _first_last_rows(ref.counts), "first and last row of every expert")
+    got = _combine_all_tokens_exact(orc, moe, c, ref, out)
     tokens = np.random.default_rng(0).choice(cfg.T, size=24, replace=False)
     tokens = np.unique(np.concatenate([tokens, [0, cfg.T - 1]]))
-    got = _combine_tokens_parity(orc, moe, c, ref, out, tokens, identity=False)
-    _end_to_end_tokens(orc, c, tokens[:8], got[:8])
+    _end_to_end_tokens(orc, c, tokens[:8], got[tokens[:8]])
     heap.destroy()
 
 
@@ -142,10 +189,12 @@ def test_decode_full(orc):
     out, code = run_path(moe, c)
     assert code == 0
     ref = _plan_and_dispatch_exact(orc, moe, c)
-    _expert_rows_parity(orc, moe, c, ref, _sample_experts(ref.counts, k=4))
+    # every row of every expert (2048 rows in all)
+    picks = {int(e): list(range(int(ref.counts[e]))) for e in np.nonzero(ref.counts)[0]}
+    _rows_parity(orc, moe, c, ref, picks, "every row of every expert")
+    got = _combine_all_tokens_exact(orc, moe, c, ref, out)
     tokens = np.arange(0, cfg.T, 17)
-    got = _combine_tokens_parity(orc, moe, c, ref, out, tokens, identity=False)
-    _end_to_end_tokens(orc, c, tokens[:6], got[:6])
+    _end_to_end_tokens(orc, c, tokens[:6], got[tokens[:6]])
     heap.destroy()
 
 
@@ -157,16 +206,17 @@ def test_mixtral_full(orc):
     out, code = run_path(moe, c)
     assert code == 0
     ref = _plan_and_dispatch_exact(orc, moe, c)
-    # a row sample per expert (first, last and a middle block of rows)
+    # the down projection splits its last tiles into K-ranges here: one row
+    # of every 256-row m-tile of every expert (a different offset in each),
+    # plus each expert's first, middle and last rows
+    picks = {}
     for e in range(cfg.E):
         n = int(ref.counts[e])
-        s, o = e // cfg.eps, int(ref.expert_off[e])
-        w13e, w2e = weights_host(c, e)
-        for r0, r1 in ((0, 3), (n // 2, n // 2 + 2), (n - 3, n)):
-            X = moe.read_rows("disp_x", s, o + r0, r1 - r0)
-            Y = moe.read_rows("out_tok", s, o + r0, r1 - r0)
-            assert_close(Y, orc.swiglu_rows(X, w13e, w2e), "expert %d rows %d:%d" % (e, r0, r1))
+        rows = [0, 1, 2, n // 2, n // 2 + 1, n - 3, n - 2, n - 1]
+        rows += [min(n - 1, m * 256 + (37 * m + 5) % 256) for m in range((n + 255) // 256)]
+        picks[e] = rows
+    _rows_parity(orc, moe, c, ref, picks, "rows of every m-tile")
+    got = _combine_all_tokens_exact(orc, moe, c, ref, out)
     tokens = np.array([0, 1, 2047, cfg.T - 1])
-    got = _combine_tokens_parity(orc, moe, c, ref, out, tokens, identity=False)
-    _end_to_end_tokens(orc, c, tokens, got)
+    _end_to_end_tokens(orc, c, tokens, got[tokens])
     heap.destroy()

@@ -273,11 +273,51 @@ def test_bad_expert_and_capacity_errors(ccm):
     heap1, moe1 = make_moe(cfg1)
     dup = np.zeros((cfg.T, 2), np.int32)  # both picks -> expert 0 -> 2T rows > cap
     c3 = make_case(cfg1, idx_w=(dup, np.full((cfg.T, 2), 0.5, np.float32)))
-    run_path(moe1, c3)
+    out3, _ = run_path(moe1, c3)
     code, st, _ = moe1.status()
     assert code == ccm.CCO_ERR_CAPACITY and st[0] == 2 * cfg.T
     assert all((g == 0xA5).all() for g in read_guards(moe1)), "overflow wrote past a window"
+    # the pairs past the slot's capacity are dropped: pos -1, as in the
+    # oracle; the rest of the path runs without them
+    from oracle import oracle as orc
+    ref = orc.pipeline(c3.x_np, c3.w_np, c3.idx_np, cfg1.E, cfg1.S, moe1.cap,
+                       bf16_bits(c3.w13), bf16_bits(c3.w2), allow_overflow=True)
+    assert ref.plan.status == orc.CAPACITY
+    pos = moe1.read_routing()[0]
+    np.testing.assert_array_equal(pos, ref.plan.pos)
+    assert (pos[cfg.T // 2:] == -1).all() and (pos[:cfg.T // 2] >= 0).all()
+    np.testing.assert_array_equal(moe1.read_rows("disp_x", 0, 0, moe1.cap), ref.disp.disp_x[0])
+    assert_close(bf16_bits(out3), ref.out, "combine after an overflow")
     heap1.destroy()
+    heap.destroy()
+
+
+def test_misaligned_pointers_are_rejected_before_any_launch(ccm):
+    from combine_symmetric_memory_amd import _capi
+    cfg = get_config("tiny")
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    lib, h = _capi.lib, moe.handle
+    INV = ccm.CCO_ERR_INVALID_ARG
+    x, w, idx = c.x.data_ptr(), c.w.data_ptr(), c.idx.data_ptr()
+    assert lib.cco_moe_plan(h, idx + 2, cfg.T, None) == INV
+    assert lib.cco_moe_plan(h, idx, cfg.T, None) == ccm.CCO_OK
+    assert lib.cco_moe_dispatch(h, x + 8, w, cfg.T, None) == INV
+    assert lib.cco_moe_dispatch(h, x, w + 2, cfg.T, None) == INV
+    assert lib.cco_moe_dispatch(h, x, w, cfg.T, None) == ccm.CCO_OK
+    w13, w2 = c.w13.data_ptr(), c.w2.data_ptr()
+    assert lib.cco_moe_expert(h, w13 + 2, w2, None) == INV
+    assert lib.cco_moe_expert(h, w13, w2 + 8, None) == INV
+    assert lib.cco_moe_expert(h, w13, w2, None) == ccm.CCO_OK
+    out = torch.empty((cfg.T + 1, cfg.H), dtype=torch.bfloat16, device="cuda")
+    o = out.data_ptr()
+    assert lib.cco_moe_combine(h, None, w, o + 2, cfg.T, None) == INV
+    assert lib.cco_moe_combine(h, None, w + 1, o, cfg.T, None) == INV
+    import ctypes
+    foreign = (ctypes.c_void_p * cfg.S)(*([moe.combine_in_view(0) + 4] + [None] * (cfg.S - 1)))
+    assert lib.cco_moe_combine(h, foreign, w, o, cfg.T, None) == INV
+    assert lib.cco_moe_combine(h, None, w, o, cfg.T, None) == ccm.CCO_OK
+    torch.cuda.synchronize()
     heap.destroy()
 
 
@@ -325,15 +365,64 @@ def test_zero_gate_gives_zero_output(ccm):
     heap.destroy()
 
 
-def test_repeated_runs_are_bit_identical(ccm):
-    cfg = get_config("tiny").with_(name="multitile", T=512, E=4, S=2, K=2, I=512, H=256)
+@pytest.mark.parametrize("H,I,E,S,K,T", [(256, 512, 4, 2, 2, 512),   # several m-tiles
+                                         (256, 2048, 2, 2, 1, 300),  # down: split K-ranges
+                                         (2048, 128, 2, 2, 1, 300),  # gate/up: split K-ranges
+                                         (512, 1024, 4, 2, 1, 400)]) # split 128-row tiles
+def test_repeated_runs_are_bit_identical(ccm, H, I, E, S, K, T):
+    """The intermediate, the expert output and combine's result repeat bit
+    for bit across runs, also where the GEMMs sum split K-ranges (fixed
+    ranges, added in range order)."""
+    cfg = get_config("tiny").with_(name="repeat", T=T, E=E, S=S, K=K, I=I, H=H)
+    say("case: repeat H=%d I=%d E=%d S=%d K=%d T=%d" % (H, I, E, S, K, T))
     c = make_case(cfg)
     heap, moe = make_moe(cfg)
-    outs = []
+    runs = []
     for _ in range(3):
         out, _ = run_path(moe, c)
-        outs.append(bf16_bits(out))
         _, st, _ = moe.status()
-    for o in outs[1:]:
-        np.testing.assert_array_equal(o, outs[0])
+        runs.append((bf16_bits(out),
+                     [moe.read_rows("hbuf", s, 0, int(st[s])) for s in range(S)],
+                     [moe.read_rows("out_tok", s, 0, int(st[s])) for s in range(S)]))
+    for o, hb, ot in runs[1:]:
+        np.testing.assert_array_equal(o, runs[0][0])
+        for s in range(S):
+            np.testing.assert_array_equal(hb[s], runs[0][1][s])
+            np.testing.assert_array_equal(ot[s], runs[0][2][s])
+    heap.destroy()
+
+
+@pytest.mark.parametrize("K,seed", [(2, 21), (4, 22), (8, 23)])
+def test_combine_bit_exact_on_rounding_ties(ccm, orc, K, seed):
+    """The kernel's combine on rows built so that every element's fp32 chain
+    ends on a binary32 rounding tie (an unfused or reordered chain gives a
+    different bf16 result; tests/combine_cases.py): bit-exact with the
+    oracle, whose chain is pinned to the exact-rational model.  The rows reach
+    combine as a foreign expert output (the copy-in fallback)."""
+    from synth import MoEConfig
+    from tests.combine_cases import _adversarial_combine_case
+    T, H, I = 64, 256, 128
+    cfg = MoEConfig(name="ties", T=T, H=H, K=K, E=K, S=2 if K % 2 == 0 else 1, I=I,
+                    routing="softmax_topk", seed=seed)
+    y, w = _adversarial_combine_case(seed, T, K, H)
+    idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))  # pair j -> expert j
+    c = make_case(cfg, idx_w=(idx, w))
+    heap, moe = make_moe(cfg)
+    ref = orc.plan(idx, cfg.E, cfg.S, moe.cap)
+    src = np.zeros((cfg.S, moe.cap, H), np.uint16)
+    eps = cfg.E // cfg.S
+    for t in range(T):
+        for j in range(K):
+            src[j // eps, ref.pos[t, j]] = y[t, j]
+    foreign = [torch.from_numpy(src[s].view(np.int16)).cuda() for s in range(cfg.S)]
+    moe.plan(c.idx)
+    moe.dispatch(c.x, c.w)
+    out, code = moe.combine(c.w, expert_out=foreign)
+    torch.cuda.synchronize()
+    assert code == ccm.CCO_INFO_COPIED
+    np.testing.assert_array_equal(moe.read_routing()[0], ref.pos)
+    want = orc.combine_tokens(src, w, idx, ref.pos, cfg.E, cfg.S)
+    got = bf16_bits(out)
+    say("  ties K=%d: %d of %d elements differ" % (K, int((got != want).sum()), got.size))
+    np.testing.assert_array_equal(got, want)
     heap.destroy()

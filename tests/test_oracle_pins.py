@@ -11,6 +11,8 @@ import torch
 
 from synth import get_config
 from synth.gen import activations, bf16_bits, bits_to_bf16, expert_weights, routing
+from tests.combine_cases import (_adversarial_combine_case, _bf16_of, _chain,
+                                 _round_rational)
 
 pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
 
@@ -163,6 +165,39 @@ def test_plan_errors(orc):
     idx = np.zeros((10, 1), np.int32)
     assert orc.plan(idx, 8, 4, 9).status == orc.CAPACITY
     assert orc.plan(idx, 8, 4, 10).status == orc.OK
+
+
+@pytest.mark.parametrize("seed,T,K,E,S,cap", [(1, 40, 3, 8, 2, 30), (2, 25, 2, 4, 4, 9),
+                                              (3, 64, 4, 8, 1, 200), (4, 7, 5, 2, 1, 20)])
+def test_plan_overflow_drops_the_rows_past_capacity(orc, seed, T, K, E, S, cap):
+    # brute force: a pair keeps the row the uncapped plan gives it when that
+    # row is inside the slot, and is dropped (-1) otherwise
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    c, o, tot, pos = _brute_plan(idx, E, S)
+    p = orc.plan(idx, E, S, cap)
+    assert p.status == (orc.CAPACITY if tot.max() > cap else orc.OK)
+    assert tot.max() > cap  # the shapes above do overflow
+    np.testing.assert_array_equal(p.counts, c)
+    np.testing.assert_array_equal(p.slot_total, tot)
+    np.testing.assert_array_equal(p.pos, np.where(pos < cap, pos, -1))
+    # dispatch and combine skip the dropped pairs
+    H = 16
+    x = _torch_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    d = orc.dispatch(x, w, idx, p.pos, E, S, cap)
+    eps = E // S
+    filled = np.zeros((S, cap), bool)
+    for t in range(T):
+        for j in range(K):
+            if p.pos[t, j] >= 0:
+                filled[idx[t, j] // eps, p.pos[t, j]] = True
+                np.testing.assert_array_equal(d.disp_x[idx[t, j] // eps, p.pos[t, j]], x[t])
+    assert (d.meta_src[~filled] == -1).all()
+    out = orc.combine_tokens(d.disp_x, w, idx, p.pos, E, S)
+    keep = np.where(p.pos >= 0, w, np.float32(0))
+    np.testing.assert_array_equal(out, orc.combine_tokens(d.disp_x, keep, idx,
+                                                          np.where(p.pos >= 0, p.pos, 0), E, S))
 
 
 # -------------------------------------------------------------- dispatch ---
@@ -385,92 +420,6 @@ def test_combine_weights_follow_columns(orc):
 # rationals, each fma rounded once to the nearest binary32 (ties to even) --
 # and the oracle must match it bit for bit, on inputs built so that the
 # unfused and the reversed chains give different bf16 results.
-
-def _round_rational(q: Fraction, prec: int, emin: int = -126) -> Fraction:
-    """Nearest number with `prec` significant bits (binary32: 24, bf16: 8) and
-    the binary32 exponent range (subnormals below 2^emin), ties to an even
-    last significand bit.  Overflow is not modelled: inputs stay finite."""
-    if q == 0:
-        return Fraction(0)
-    sign = -1 if q < 0 else 1
-    a = abs(q)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if Fraction(2) ** e > a:
-        e -= 1
-    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
-    quantum = Fraction(2) ** (max(e, emin) - (prec - 1))
-    n = a / quantum
-    lo = n.numerator // n.denominator
-    rest = n - lo
-    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and lo % 2 == 1):
-        lo += 1
-    return sign * lo * quantum
-
-
-def _bf16_of(q: Fraction) -> int:
-    """bf16 bit pattern of a rational that is exactly a bf16 value."""
-    f = np.float32(float(q))
-    assert Fraction(float(f)) == q
-    return int(np.array([f], np.float32).view(np.uint32)[0]) >> 16
-
-
-def _chain(w_row, y_rows, h, fused=True, reverse=False):
-    """bf16 bits of one output element: acc = 0; acc = fma(w_j, y_j[h], acc)
-    over j (fused: one rounding per step; unfused: the product is rounded
-    first), then one rounding to bf16."""
-    acc = Fraction(0)
-    order = range(len(w_row) - 1, -1, -1) if reverse else range(len(w_row))
-    for j in order:
-        prod = Fraction(float(w_row[j])) * Fraction(float(_f32(y_rows[j][h:h + 1])[0]))
-        if not fused:
-            prod = _round_rational(prod, 24)
-        acc = _round_rational(prod + acc, 24)
-    return _bf16_of(_round_rational(acc, 8))
-
-
-def _adversarial_combine_case(seed: int, nt: int, K: int, H: int):
-    """Rows and weights whose fp32 chains end on a binary32 rounding tie.
-
-    Column 0 puts the accumulator on a bf16 midpoint m (w0 = m, y0 = a power
-    of two per element).  One later column c adds the product w_c * y_c =
-    (1 + eps) * ulp32(m) / 2 with 0 < eps < 2^-24: a fused step keeps eps and
-    rounds m + ulp32/2 up, while a product rounded first loses it and the tie
-    goes to even (m, whose last binary32 bit is 0).  The final bf16 rounding
-    of m is itself a tie, so half of the elements end one bf16 ulp apart.
-    The other columns have zero weights, which leave a fused chain exact.
-    Reversed, the chain adds the rounded product to m last: the unfused
-    result again."""
-    rng = np.random.default_rng(seed)
-    y = np.zeros((nt, K, H), np.uint16)
-    w = np.zeros((nt, K), np.float32)
-    for q in range(nt):
-        while True:
-            ex = int(rng.integers(-20, 20))
-            mant = int(rng.integers(0x80, 0x100))
-            m = (mant + 0.5) * 2.0 ** (ex - 7)  # a bf16 midpoint, 9 significant bits
-            sgn = 1.0 if rng.random() < 0.5 else -1.0
-            ulp32 = 2.0 ** (np.floor(np.log2(m)) - 23)
-            yc = 1.0 + int(rng.integers(1, 128)) / 128.0  # bf16 with low bits
-            half = ulp32 / 2
-            wc = np.float32(half / yc)
-            if Fraction(float(wc)) * Fraction(yc) <= Fraction(half):
-                wc = np.nextafter(wc, np.float32(np.inf))
-            eps = Fraction(float(wc)) * Fraction(yc) / Fraction(half) - 1
-            if 0 < eps < Fraction(1, 2 ** 24):
-                break
-        c = int(rng.integers(1, K)) if K > 1 else 0
-        assert K > 1
-        w[q, 0] = np.float32(sgn * m)
-        w[q, c] = np.float32(sgn * float(wc))
-        for h in range(H):
-            k2 = int(rng.integers(-3, 4))
-            y[q, 0, h] = _torch_bf16_bits(np.array([2.0 ** k2], np.float32))[0]
-            y[q, c, h] = _torch_bf16_bits(np.array([yc * 2.0 ** k2], np.float32))[0]
-            for j in range(1, K):
-                if j != c:
-                    y[q, j, h] = _torch_bf16_bits(rng.standard_normal(1).astype(np.float32))[0]
-    return y, w
-
 
 def _random_combine_case(seed: int, nt: int, K: int, H: int):
     rng = np.random.default_rng(seed)
