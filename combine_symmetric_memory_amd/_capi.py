@@ -19,6 +19,7 @@ CCO_ERR_HIP = -3
 CCO_ERR_CAPACITY = -4
 CCO_ERR_BAD_EXPERT = -5
 CCO_ERR_HEAP_FULL = -6
+CCO_ERR_TOO_LARGE = -7
 CCO_NUM_KERNEL_KINDS = 8
 KERNEL_KINDS = ("plan_count", "plan_rank", "dispatch", "expert_gate_up", "expert_down",
                 "combine", "combine_copy_in", "dispatch_fp8")
@@ -69,6 +70,8 @@ SIGNATURES = [
     ("cco_moe_status", ctypes.c_int, [P, P, P, P]),
     ("cco_moe_set_timing", ctypes.c_int, [P, ctypes.c_int]),
     ("cco_moe_timing_summary", ctypes.c_int, [P, P, P]),
+    ("cco_moe_plan_noalloc", ctypes.c_int, [P, I32, I32, I32, I32, ctypes.c_int64, P, P, P,
+                                             P, P, P]),
     ("cco_status_string", ctypes.c_char_p, [ctypes.c_int]),
 ]
 

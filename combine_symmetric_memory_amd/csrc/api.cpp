@@ -184,6 +184,7 @@ const char *cco_status_string(int st) {
     case CCO_ERR_CAPACITY: return "CCO_ERR_CAPACITY";
     case CCO_ERR_BAD_EXPERT: return "CCO_ERR_BAD_EXPERT";
     case CCO_ERR_HEAP_FULL: return "CCO_ERR_HEAP_FULL";
+    case CCO_ERR_TOO_LARGE: return "CCO_ERR_TOO_LARGE";
     default: return "unknown cco status";
   }
 }

@@ -58,7 +58,8 @@ typedef enum {
   CCO_ERR_HIP = -3,            /* a HIP runtime call failed */
   CCO_ERR_CAPACITY = -4,       /* device: a slot received more than cap rows */
   CCO_ERR_BAD_EXPERT = -5,     /* device: an expert id outside [0, E) */
-  CCO_ERR_HEAP_FULL = -6       /* the heap's slots have no room for this object */
+  CCO_ERR_HEAP_FULL = -6,      /* the heap's slots have no room for this object */
+  CCO_ERR_TOO_LARGE = -7       /* the batch exceeds the fixed scratch of cco_moe_plan_noalloc */
 } cco_status;
 
 /* Opaque handles. */
@@ -270,6 +271,32 @@ int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weig
  * CCO_ERR_BAD_EXPERT or CCO_ERR_CAPACITY), CCO_ERR_INVALID_ARG for a NULL
  * m, or CCO_ERR_HIP. */
 int cco_moe_status(cco_moe *m, void *stream, int32_t *slot_total, int32_t *expert_counts);
+
+/* The plan of cco_moe_plan, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, hosts that forbid
+ * allocation): no cco_moe object, every output in caller memory, and the
+ * kernels' scratch (per-chunk histograms, a chunk ticket, each pair's
+ * expert id) in a fixed array of about 3 MiB that the library holds on each
+ * GPU it runs on until the process ends.  Calls nothing that allocates.
+ *   topk_idx    device int32 [T][K] expert ids (may be NULL when T == 0)
+ *   T, K, E, S  tokens, top-k (1..32), experts (1..1024), slots (E % S == 0)
+ *   cap         rows per slot (0 <= cap <= INT32_MAX); a pair whose row
+ *               would fall at or past cap gets pos -1 and the status word
+ *               CCO_ERR_CAPACITY
+ *   pos         device int32 [T][K] (may be NULL when T == 0)
+ *   counts, expert_off  device int32 [E];  slot_total  device int32 [S]
+ *   status      device int32 [1]: CCO_OK, CCO_ERR_BAD_EXPERT or
+ *               CCO_ERR_CAPACITY once the stream reaches it
+ * Outputs are those cco_moe_plan writes for the same idx, S and cap.  All
+ * pointers 4-byte aligned; runs on the current device, asynchronously on
+ * `stream`.  Errors, before any launch: CCO_ERR_TOO_LARGE for T * K above
+ * 2^19 pairs; CCO_ERR_INVALID_ARG for the other limits and for NULL or
+ * misaligned pointers.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (two streams or two host threads) race, so
+ * serialise them. */
+int cco_moe_plan_noalloc(const int32_t *topk_idx, int32_t T, int32_t K, int32_t E, int32_t S,
+                         int64_t cap, int32_t *pos, int32_t *counts, int32_t *expert_off,
+                         int32_t *slot_total, int32_t *status, void *stream);
 
 /* Per-kernel timing with HIP events on the launch stream.  While enabled,
  * each kernel launch of this object is bracketed by a pair of events; the
