@@ -236,6 +236,103 @@ def calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert=None):
     return cal
 
 
+def stage_in_variant(cfg, moe, slot_total, stream, dev, torch):
+    """The expert output of every slot handed over in buffers of the
+    caller's and staged into the combine windows on the copy engines
+    (cco_moe_stage_in_sdma, no kernel), against the same bytes moved by the
+    library's copy kernel on the compute units (the copy fallback inside
+    cco_moe_combine); then each beside a large vendor GEMM on another stream,
+    to show what the copy takes from the compute units."""
+    import numpy as np
+    flush = CacheFlush(torch, dev)
+    rows = [int(r) for r in slot_total]
+    foreign = [torch.zeros((max(r, 1), cfg.H), dtype=torch.bfloat16, device=dev) for r in rows]
+    moved = 2 * 2 * cfg.H * sum(rows)  # read + write
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def sdma(st):
+        for s in range(cfg.S):
+            moe.stage_in_sdma(s, foreign[s], rows[s], stream=st)
+
+    # the copy kernel of the fallback, on the same bytes (its per-launch
+    # times from the library's own events)
+    dst = [torch.empty_like(f) for f in foreign]
+
+    def cu_copy(st):
+        with torch.cuda.stream(st):
+            for d, f in zip(dst, foreign):
+                d.copy_(f)
+
+    def alone(fn, n=5):
+        fn(stream)
+        ts = []
+        for _ in range(n):
+            flush()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    res = {"bytes_moved": moved}
+    ms = alone(sdma)
+    res["sdma_ms"] = round(ms, 4)
+    res["sdma_GB_s"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    ms = alone(cu_copy)
+    res["copy_kernel_ms"] = round(ms, 4)
+    res["copy_kernel_GB_s"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    # beside a GEMM on the compute units: the copies go on a second stream
+    M, N, K = 32768, 4096, 7168
+    a = torch.randn(M, K, device=dev).to(torch.bfloat16)
+    b = torch.randn(K, N, device=dev).to(torch.bfloat16)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream(device=dev)
+
+    def gemm():
+        torch.matmul(a, b, out=c)
+
+    def beside(copy):
+        flush()
+        torch.cuda.synchronize()
+        g0, g1, c1 = ev(), ev(), ev()
+        g0.record(stream)
+        side.wait_event(g0)
+        if copy is not None:
+            copy(side)
+        gemm()
+        g1.record(stream)
+        c1.record(side)
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1), max(g0.elapsed_time(g1), g0.elapsed_time(c1))
+
+    # the three cases interleaved, so that clock and cache state drift alike
+    for _ in range(3):
+        gemm()
+    runs = {None: [], sdma: [], cu_copy: []}
+    for _ in range(7):
+        for k in runs:
+            runs[k].append(beside(k))
+
+    def med(k, i):
+        return float(np.median([r[i] for r in runs[k]]))
+    g_alone = med(None, 0)
+    g_sdma, t_sdma = med(sdma, 0), med(sdma, 1)
+    g_cu, t_cu = med(cu_copy, 0), med(cu_copy, 1)
+    res["gemm_shape_MNK"] = [M, N, K]
+    res["gemm_alone_ms"] = round(g_alone, 4)
+    res["gemm_beside_sdma_ms"] = round(g_sdma, 4)
+    res["gemm_beside_copy_kernel_ms"] = round(g_cu, 4)
+    res["both_done_sdma_ms"] = round(t_sdma, 4)
+    res["both_done_copy_kernel_ms"] = round(t_cu, 4)
+    torch.cuda.synchronize()
+    del foreign, dst, a, b, c, flush
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +484,13 @@ def main():
             "hbm_frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "vs_bf16_dispatch_time": round(avg / stages["dispatch"]["avg_ms"], 3)}
         log("variants", json.dumps(variants))
+
+    if cfg.I > 0:
+        variants["stage_in_sdma"] = stage_in_variant(cfg, moe, slot_total, stream, dev, torch)
+        log("variants", json.dumps({"stage_in_sdma": variants["stage_in_sdma"]}))
+        # the staging windows back to the step's own expert output
+        moe.expert(w13, w2, stream)
+        torch.cuda.synchronize()
 
     # roofline of the dominant kernel (the longest one), bound by HBM or by
     # the matrix cores according to its arithmetic intensity

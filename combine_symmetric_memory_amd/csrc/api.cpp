@@ -506,6 +506,26 @@ int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weig
   return copied ? CCO_INFO_COPIED : CCO_OK;
 }
 
+int cco_moe_stage_in_sdma(cco_moe *m, int32_t slot, const void *src, int32_t rows,
+                          void *stream) {
+  if (!m || slot < 0 || slot >= m->S || rows < 0 || (int64_t)rows > m->cap) return CCO_ERR_INVALID_ARG;
+  if (rows == 0) return CCO_OK;
+  if (!src || !aligned(src, 16)) return CCO_ERR_INVALID_ARG;
+  char *dst = (char *)cco_moe_combine_in_view(m, slot);
+  if (src == dst) return CCO_OK;  // already the staging view
+  const uint64_t n = (uint64_t)rows * (uint64_t)m->shape.hidden * 2;
+  const char *s = (const char *)src;
+  if (s < dst + n && dst < s + n) return CCO_ERR_INVALID_ARG;
+  DeviceGuard dg(m->heap->device);
+  if (!dg.ok) return CCO_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  // hipMemcpyDeviceToDeviceNoCU: a device-to-device copy on the copy
+  // engines, with no kernel on the compute units
+  return timed_launch(m, 8, st, [&] {
+    return hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDeviceNoCU, st);
+  });
+}
+
 int cco_moe_status(cco_moe *m, void *stream, int32_t *slot_total, int32_t *expert_counts) {
   if (!m) return CCO_ERR_INVALID_ARG;
   DeviceGuard dg(m->heap->device);

@@ -255,6 +255,17 @@ class MoE:
         check(code, "cco_moe_combine", allow=(_capi.CCO_OK, _capi.CCO_INFO_COPIED))
         return out, code
 
+    def stage_in_sdma(self, slot: int, src: torch.Tensor | int, rows: int, stream=None) -> None:
+        """cco_moe_stage_in_sdma: rows of `src` (bf16 [rows, H] tensor or a
+        device address) into slot's staging window on the copy engines."""
+        if isinstance(src, torch.Tensor):
+            if src.dtype != torch.bfloat16 or src.dim() != 2 or src.shape[1] != self.H or \
+               src.shape[0] < rows or not src.is_contiguous():
+                raise ValueError("src must be a contiguous bf16 [>= rows, H] tensor")
+            src = src.data_ptr()
+        check(lib.cco_moe_stage_in_sdma(self.handle, int(slot), ctypes.c_void_p(int(src)),
+                                        int(rows), _stream(stream)), "cco_moe_stage_in_sdma")
+
     def status(self, stream=None):
         """cco_moe_status -> (code, slot_total [S], counts [E]) (synchronises)."""
         st = np.zeros(self.S, np.int32)

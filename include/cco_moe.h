@@ -259,6 +259,27 @@ void *cco_moe_combine_in_view(cco_moe *m, int32_t slot);
 int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weights,
                     uint16_t *out, int32_t T, void *stream);
 
+/* Copy one slot's expert output from a buffer of the caller's into that
+ * slot's combine staging window on the GPU's copy engines (SDMA), not on
+ * compute units ([blog] "Multiple communication transports": SDMA serves
+ * background bulk copies that keep the CUs free; "GEMM + all-to-all
+ * fusion": GEMM output tiles move by SDMA as they become ready, while the
+ * remaining tiles compute).  A caller whose expert writes buffers of its own
+ * (the pages' data_ptr mismatch, [blog] "Zero-copy MoE dispatch", note)
+ * issues this per slot, on a stream of its own, as each slot's output is
+ * done, and then calls cco_moe_combine with expert_out = NULL.
+ *   slot    0 <= slot < S
+ *   src     device bf16 [rows][H], 16-byte aligned, not overlapping the
+ *           window (src equal to the staging view copies nothing)
+ *   rows    rows to copy, 0 <= rows <= cap: the slot's receive count, which
+ *           the caller holds (cco_moe_status; the pages' total_recv).  Rows
+ *           of the window past `rows` keep what they held, so a count below
+ *           the receive count leaves combine reading stale rows.
+ * Asynchronous on `stream`.  Errors: CCO_ERR_INVALID_ARG (before any copy),
+ * CCO_ERR_HIP. */
+int cco_moe_stage_in_sdma(cco_moe *m, int32_t slot, const void *src, int32_t rows,
+                          void *stream);
+
 /* Receive counts and device status, read on the host ([blog] "Zero-copy
  * MoE dispatch -> expert -> combine", step 1: after dispatch the host
  * synchronises and reads the device-side receive count, total_recv, to
@@ -304,9 +325,9 @@ int cco_moe_plan_noalloc(const int32_t *topk_idx, int32_t T, int32_t K, int32_t 
  * total milliseconds (kinds: 0 plan-count (the whole plan for a batch of
  * at most 2048 (token, k) pairs, which runs in one launch), 1 plan-rank, 2 dispatch,
  * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in,
- * 7 8-bit dispatch).
+ * 7 8-bit dispatch, 8 staging copy on the copy engines).
  * Reading the summary synchronises the recorded events and resets it. */
-#define CCO_NUM_KERNEL_KINDS 8
+#define CCO_NUM_KERNEL_KINDS 9
 int cco_moe_set_timing(cco_moe *m, int enable);
 int cco_moe_timing_summary(cco_moe *m, int32_t *launches, double *total_ms);
 

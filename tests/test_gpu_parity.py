@@ -426,3 +426,45 @@ def test_combine_bit_exact_on_rounding_ties(ccm, orc, K, seed):
     say("  ties K=%d: %d of %d elements differ" % (K, int((got != want).sum()), got.size))
     np.testing.assert_array_equal(got, want)
     heap.destroy()
+
+
+def test_stage_in_on_the_copy_engines(ccm):
+    """cco_moe_stage_in_sdma: a foreign expert output staged slot by slot on
+    the copy engines, then combine through the views, equals the zero-copy
+    combine bit for bit; bad arguments are rejected before any copy."""
+    cfg = get_config("tiny").with_(name="stage", T=512, E=8, S=4, K=2, I=512, H=256)
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    out0, code = run_path(moe, c)
+    assert code == ccm.CCO_OK
+    _, st, _ = moe.status()
+    H = cfg.H
+    foreign = [torch.from_numpy(moe.read_rows("out_tok", s, 0, int(st[s])).view(np.int16))
+               .view(torch.bfloat16).cuda() for s in range(cfg.S)]
+    zeros = torch.zeros((moe.cap, H), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for s in range(cfg.S):
+            moe.stage_in_sdma(s, zeros, moe.cap, stream=side)  # clear the whole window
+    torch.cuda.synchronize()
+    assert not moe.read_rows("out_tok", 0, 0, int(st[0])).any()
+    with torch.cuda.stream(side):
+        for s in range(cfg.S):
+            moe.stage_in_sdma(s, foreign[s], int(st[s]), stream=side)
+    torch.cuda.synchronize()
+    out1, code1 = moe.combine(c.w)
+    torch.cuda.synchronize()
+    assert code1 == ccm.CCO_OK
+    np.testing.assert_array_equal(bf16_bits(out1), bf16_bits(out0))
+    from combine_symmetric_memory_amd import _capi
+    lib, h, INV = _capi.lib, moe.handle, ccm.CCO_ERR_INVALID_ARG
+    f0 = foreign[0].data_ptr()
+    assert lib.cco_moe_stage_in_sdma(h, cfg.S, f0, 1, None) == INV
+    assert lib.cco_moe_stage_in_sdma(h, -1, f0, 1, None) == INV
+    assert lib.cco_moe_stage_in_sdma(h, 0, f0, moe.cap + 1, None) == INV
+    assert lib.cco_moe_stage_in_sdma(h, 0, f0 + 2, 1, None) == INV
+    view = moe.combine_in_view(0)
+    assert lib.cco_moe_stage_in_sdma(h, 0, view + 16 * H, 64, None) == INV  # overlaps
+    assert lib.cco_moe_stage_in_sdma(h, 0, view, 64, None) == ccm.CCO_OK     # the view itself
+    torch.cuda.synchronize()
+    heap.destroy()
