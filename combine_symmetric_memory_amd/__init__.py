@@ -8,10 +8,13 @@ binding.  Importing it without the built library raises ImportError.
 from ._capi import (  # noqa: F401
     CCO_ERR_BAD_EXPERT,
     CCO_ERR_CAPACITY,
+    CCO_ERR_DISABLED,
     CCO_ERR_HEAP_FULL,
     CCO_ERR_HIP,
     CCO_ERR_INVALID_ARG,
     CCO_ERR_OUT_OF_MEMORY,
+    CCO_ERR_TIMEOUT,
+    CCO_ERR_TOO_LARGE,
     CCO_INFO_COPIED,
     CCO_OK,
     KERNEL_KINDS,

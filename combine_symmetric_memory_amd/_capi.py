@@ -20,9 +20,11 @@ CCO_ERR_CAPACITY = -4
 CCO_ERR_BAD_EXPERT = -5
 CCO_ERR_HEAP_FULL = -6
 CCO_ERR_TOO_LARGE = -7
-CCO_NUM_KERNEL_KINDS = 9
+CCO_ERR_TIMEOUT = -8
+CCO_ERR_DISABLED = -9
+CCO_NUM_KERNEL_KINDS = 10
 KERNEL_KINDS = ("plan_count", "plan_rank", "dispatch", "expert_gate_up", "expert_down",
-                "combine", "combine_copy_in", "dispatch_fp8", "stage_in_sdma")
+                "combine", "combine_copy_in", "dispatch_fp8", "stage_in_sdma", "fused")
 
 
 class cco_moe_shape(ctypes.Structure):
@@ -67,6 +69,7 @@ SIGNATURES = [
     ("cco_moe_dispatch_view", P, [P, I32]),
     ("cco_moe_combine_in_view", P, [P, I32]),
     ("cco_moe_combine", ctypes.c_int, [P, P, P, P, I32, P]),
+    ("cco_moe_fused", ctypes.c_int, [P, P, P, P, P, P, P, I32, P]),
     ("cco_moe_stage_in_sdma", ctypes.c_int, [P, I32, P, I32, P]),
     ("cco_moe_status", ctypes.c_int, [P, P, P, P]),
     ("cco_moe_set_timing", ctypes.c_int, [P, ctypes.c_int]),

@@ -65,6 +65,7 @@ struct cco_moe {
   int32_t planned_T = -1;  // T of the last plan (host-side order check)
   bool disp_8bit = false;  // the last dispatch moved 8-bit tokens with scales
   int num_cus = 0;
+  cco::FusedBuffers fused{};
   bool timing = false;
   std::vector<TimedPair> pending[CCO_NUM_KERNEL_KINDS];
   int32_t timed_launches[CCO_NUM_KERNEL_KINDS] = {};
@@ -185,6 +186,8 @@ const char *cco_status_string(int st) {
     case CCO_ERR_BAD_EXPERT: return "CCO_ERR_BAD_EXPERT";
     case CCO_ERR_HEAP_FULL: return "CCO_ERR_HEAP_FULL";
     case CCO_ERR_TOO_LARGE: return "CCO_ERR_TOO_LARGE";
+    case CCO_ERR_TIMEOUT: return "CCO_ERR_TIMEOUT";
+    case CCO_ERR_DISABLED: return "CCO_ERR_DISABLED";
     default: return "unknown cco status";
   }
 }
@@ -293,8 +296,11 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   // split tiles' partial sums, 256-byte aligned
   const int nwg = cco::gemm_workgroups(m->num_cus);
   const size_t n_desc = (size_t)(nwg / 2) * cco::kSplitDescInts;
+  const size_t n_mt = (size_t)cco::fused_mtiles(shape->max_tokens, shape->topk, E);
+  const size_t n_fused = cco::kFusedCounterWords + 3 * (size_t)(E + 1) + E + 2 * n_mt;
   const size_t n_head = (size_t)npairs * 2 + (size_t)E * 2 + (size_t)m->S + 2 +
-                        4 * (cco::kNumXcd + 1) + n_desc + (size_t)m->max_plan_blocks * (E + 1);
+                        4 * (cco::kNumXcd + 1) + n_desc + (size_t)m->max_plan_blocks * (E + 1) +
+                        n_fused;
   const size_t ws_at = (n_head + 63) / 64 * 64;
   const size_t n_ws = shape->inter > 0 ? (size_t)nwg * cco::kSplitTileFloats : 0;
   const size_t n_i32 = ws_at + n_ws;
@@ -334,6 +340,13 @@ int cco_moe_create(cco_sym_heap *heap, const cco_moe_shape *shape, cco_moe **out
   a.ticket = p;            p += 1;
   a.gemm_queue = p;        p += 4 * (cco::kNumXcd + 1);
   a.split_desc = p;        p += n_desc;
+  m->fused.q = p;          p += cco::kFusedCounterWords;
+  m->fused.pre_g = p;      p += E + 1;
+  m->fused.pre_w = p;      p += E + 1;
+  m->fused.pre_mt = p;     p += E + 1;
+  m->fused.arrived = p;    p += E;
+  m->fused.gu_done = p;    p += n_mt;
+  m->fused.dn_done = p;    p += n_mt;
   a.hist = p;
   a.split_ws = n_ws ? (float *)((int32_t *)st + ws_at) : nullptr;
 
@@ -504,6 +517,39 @@ int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weig
   });
   if (rc != CCO_OK) return rc;
   return copied ? CCO_INFO_COPIED : CCO_OK;
+}
+
+int cco_moe_fused(cco_moe *m, const int32_t *topk_idx, const uint16_t *x, const float *weights,
+                  const uint16_t *w13, const uint16_t *w2, uint16_t *out, int32_t T,
+                  void *stream) {
+  if (!m || T < 0 || T > m->shape.max_tokens) return CCO_ERR_INVALID_ARG;
+  if (m->shape.topk > 8) return CCO_ERR_INVALID_ARG;  // the single launch takes top-k <= 8
+  if (T > 0 && (!topk_idx || !x || !weights || !out)) return CCO_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned(topk_idx, 4) || !aligned(x, 16) || !aligned(weights, 4) ||
+                !aligned(out, 16)))
+    return CCO_ERR_INVALID_ARG;
+  if (m->shape.inter > 0 && (!w13 || !w2 || !aligned(w13, 16) || !aligned(w2, 16)))
+    return CCO_ERR_INVALID_ARG;
+  if (T == 0) {
+    // nothing to move: the plan of an empty batch (zero counts)
+    const int rc = cco_moe_plan(m, topk_idx, 0, stream);
+    if (rc == CCO_OK) m->disp_8bit = false;
+    return rc;
+  }
+  DeviceGuard dg(m->heap->device);
+  if (!dg.ok) return CCO_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  MoeArgs a = m->args;
+  hipError_t err = hipSuccess;
+  const int rc = timed_launch(m, 9, st, [&] {
+    err = cco::launch_fused(a, m->fused, topk_idx, x, weights, w13, w2, out, T, m->num_cus, st);
+    return err;
+  });
+  if (err == hipErrorNotSupported) return CCO_ERR_DISABLED;  // not built (see fused.hip)
+  if (rc != CCO_OK) return rc;
+  m->planned_T = T;
+  m->disp_8bit = false;
+  return CCO_OK;
 }
 
 int cco_moe_stage_in_sdma(cco_moe *m, int32_t slot, const void *src, int32_t rows,

@@ -114,6 +114,30 @@ hipError_t launch_combine(const MoeArgs &a, uint64_t src_win, const float *w,
 hipError_t launch_copy_in(const MoeArgs &a, int32_t slot, const uint16_t *src,
                           uint64_t dst_win, hipStream_t st);
 
+// State of the single-launch path (fused.hip), part of the routing state:
+// counters (zero between launches) and per-launch tables.
+constexpr int kFusedCounterWords = 64;
+struct FusedBuffers {
+  int32_t *q;        // [kFusedCounterWords]
+  int32_t *pre_g;    // [E + 1]
+  int32_t *pre_w;    // [E + 1]
+  int32_t *pre_mt;   // [E + 1]
+  int32_t *arrived;  // [E]
+  int32_t *gu_done;  // [fused_mtiles]
+  int32_t *dn_done;  // [fused_mtiles]
+};
+// 256-row m-tiles of all experts together: sum over e of ceil(rows_e / 256)
+// <= T * K / 256 + E.
+inline int64_t fused_mtiles(int64_t max_tokens, int K, int E) {
+  return E + (max_tokens * K + 255) / 256;
+}
+// The whole path (plan, dispatch, both expert GEMMs, combine) in one
+// persistent launch of one workgroup per CU.
+hipError_t launch_fused(const MoeArgs &a, const FusedBuffers &b, const int32_t *idx,
+                        const uint16_t *x, const float *w, const uint16_t *w13,
+                        const uint16_t *w2, uint16_t *out, int32_t T, int num_cus,
+                        hipStream_t st);
+
 // Expert GEMMs of the T planned tokens.  `num_cus` sizes the persistent
 // grids.
 hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int32_t T, int num_cus,

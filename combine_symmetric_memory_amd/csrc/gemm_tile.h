@@ -1,0 +1,620 @@
+// gemm_tile.h -- one tile of the grouped expert GEMMs on gfx950 bf16 MFMA,
+// and the per-expert tile list.  Included by expert.hip (the grouped GEMM
+// launches) and fused.hip (the single-launch path); everything here has
+// internal linkage.
+//
+// "MORI CCO: Next-Generation Collective Communication Object for GPUs",
+// section "Zero-copy MoE dispatch -> expert -> combine", step 2: the expert
+// GEMM reads its rows in place from the receive window and writes its output
+// straight into the combine staging window, row i for row i.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
+#include "cco_internal.h"
+
+namespace cco {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32, which
+// the compiler emits for a plain conversion (two values per instruction).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// silu(z) = z / (1 + e^-z); the reciprocal is the hardware's (about 1 ulp of
+// fp32), far below the bf16 rounding that follows.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+struct GemmDesc {
+  uint64_t a_win;        // A rows: window of the expert's slot, row stride lda
+  int32_t lda;
+  const uint16_t *w;     // B: weights of expert 0; expert e at w + e * w_estride
+  int64_t w_estride;
+  int64_t w_bytes;       // bytes of one expert's weight matrix
+  int32_t ldb;
+  uint64_t c_win;        // C rows: window of the expert's slot, row stride ldc
+  int32_t ldc;
+  int32_t kdim;          // reduction length
+  int32_t ntiles;        // tiles along N
+  int32_t up_off;        // gate/up: first row of the up projection (= I)
+  int32_t *queue;        // [kNumXcd] next-tile counters + [1] exit counter
+  int32_t allow_split;   // nonzero: the tail and fixup launches follow this GEMM
+  float *split_ws;       // fp32 partial sums of split tiles: one slot per workgroup
+  int32_t *split_desc;   // [workgroups / 2][kSplitDescInts] split tiles, kind 0 = free
+};
+
+// Rows of expert e that fit its slot (a slot overflow is reported by the
+// plan; the rows past the capacity were never written).
+__device__ __forceinline__ int rows_of(const MoeArgs &a, int e) {
+  const int64_t off = a.expert_off[e];
+  int64_t n = a.counts[e];
+  if (off + n > a.cap) n = a.cap - off;
+  return n > 0 ? (int)n : 0;
+}
+
+// Wait until at most N vector-memory operations (the direct-to-LDS loads
+// included) / at most N LDS reads of this wavefront are in flight.  LDS
+// reads return in order, so a partial lgkmcnt wait names a prefix of them.
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8), issued through the builtin so that the
+// compiler's own wait insertion sees them.  Both are scheduling barriers
+// too: no instruction moves across a wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// waits for every outstanding load, prefetches of later stages included.
+// Callers order their own LDS traffic with explicit vmcnt waits.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+
+// A wavefront-uniform value the compiler cannot prove uniform (it came from
+// memory) moved into scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char *uniform(const char *p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// LDS byte address (as the ds_* instructions see it) of a shared pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_char_t *)p;
+}
+
+// Buffer resource of a raw byte range (stride 0, 32-bit dword format word
+// of the gfx9 family); loads past num_bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range_rsrc(const void *base,
+                                                                  uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+
+// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes, read at
+// byte voff (per lane) + soff (wavefront-uniform) of the range, land at
+// lds_base + 16 * l (lds_base wavefront-uniform).  Only scalar work besides
+// the load itself: the offsets are registers the caller keeps.
+__device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   uint32_t soff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, (int)soff,
+                                           0, 0);
+}
+
+// LDS tile layout: rows of BK bf16 (ROWB bytes), unpadded, 16-byte chunks
+// XOR-swizzled per row so that the 16 rows one fragment read touches fall
+// on distinct bank groups: physical chunk = logical chunk ^ swz(row).
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  return (row / (16 / CPR)) % CPR;
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time
+// indices for register arrays).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Full tile 256 x 256 x 32 with a 5-deep ring (32 KiB stages); the 128 x 512
+// remainder tile (40 KiB stages) with 4.  Either ring fills the 160 KiB of
+// LDS, so the kernel keeps nothing else there.
+constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 5, kStagesHalf = 4;
+
+// Wavefronts per workgroup: one per SIMD.
+constexpr int kGemmWaves = 4;
+
+// Split of a short last round: a tile cut into K-ranges keeps at least this
+// many K-steps per range.  Each range's fp32 partial sums take one
+// workspace slot of kSplitTileFloats (either tile shape has that many
+// accumulators).
+constexpr int kMinSplitSteps = 8;
+// Only GEMMs of fewer rounds than this split their last one: with more,
+// the short round is a small part of the time, and the dynamic hand-out
+// already fills much of it.
+constexpr int kSplitMaxRounds = 4;
+static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTileFloats,
+              "a workspace slot holds one tile's accumulators");
+
+// Tile: BM rows x BN columns of one expert on 4 wavefronts, one per SIMD,
+// each owning a 128 x 128 block of the output as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 with the accumulators in AGPRs.  Wavefront w sits
+// at (wm, wn) = (w / WN, w % WN) of a WM x WN grid; its row blocks are
+// wm, wm + WM, wm + 2 WM, ... (interleaved, so a partly empty tile still
+// splits evenly) and its columns [wn * 128, wn * 128 + 128).
+//
+// The LDS operand reads set the pace: a SIMD moves about 26 bytes per clock
+// from LDS into registers, and a 4 x 4 block tile needs 8 fragment reads per
+// 16 MFMAs (1 KiB each) -- half an MFMA's worth of time per read, which the
+// MFMAs hide.  (Two wavefronts per SIMD halve the register budget; 4 x 2
+// block tiles then need 12 reads per 16 MFMAs, more than the matrix core's
+// time covers.)
+//
+// Both operands go global -> LDS through a STAGES-deep ring of direct
+// 16-byte-per-lane buffer loads (XOR-swizzled rows, free of bank conflicts).
+// A K-step of 32 is two MFMA sub-steps; while one sub-step's MFMAs run, the
+// wavefront reads the next sub-step's fragments and issues its share of a
+// later stage's loads between them.  One barrier per K-step, between its
+// two sub-steps, makes the next stage visible to every wavefront and frees
+// the ring slot of the previous one.
+//
+// n_tile counts BN-wide column tiles (for gate/up: BN/2 intermediate
+// columns, gate and up interleaved in 32-row blocks); rows [row0, row0 +
+// rows_valid) of expert e are computed over the nkt K-steps from kb on.
+// With part == nullptr the result goes to the expert's output rows;
+// otherwise the fp32 sums of this K-range are written to part, row-major
+// [BM][BN] in the accumulators' column order.  Every wavefront of the
+// workgroup calls this with the same arguments.
+template <int BM, int BN, int STAGES, bool SWIGLU>
+__device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
+                                         int n_tile, int row0, int rows_valid, int lag, int kb,
+                                         int nkt, float *part) {
+  constexpr int BK = kBK;
+  constexpr int NW = kGemmWaves;
+  constexpr int WM = BM / 128;          // wavefront rows
+  constexpr int WN = NW / WM;           // wavefront columns
+  constexpr int TN = BN / WN;           // columns per wavefront
+  constexpr int FN = TN / 32;           // 32-column blocks per wavefront
+  constexpr int MB = BM / 32;           // 32-row blocks per tile
+  constexpr int FM = MB / WM;           // 32-row blocks per wavefront
+  constexpr int ROWB = BK * 2;          // bytes per LDS row
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;      // rows filled by one 1 KiB wavefront load
+  constexpr int A_BYTES = BM * ROWB;
+  constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  constexpr int LA = BM / (RPI * NW);   // A loads per wavefront per stage
+  constexpr int LB = BN / (RPI * NW);   // B loads per wavefront per stage
+  constexpr int LPS = LA + LB;
+  constexpr int KSUB = BK / 16;         // MFMA sub-steps per K-step
+  static_assert(WM * WN == NW && FM == 4 && FN == 4, "4 x 4 blocks of 32 x 32 per wavefront");
+  static_assert(KSUB == 2, "a K-step is two MFMA sub-steps");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
+  static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
+  static_assert(STAGES >= 3 && (STAGES - 2) * LPS < 64, "stage count / vmcnt range");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  // the tile's parameters are wavefront-uniform; keep them (and the operand
+  // descriptors built from them) in scalar registers
+  e = uniform(e);
+  n_tile = uniform(n_tile);
+  row0 = uniform(row0);
+  rows_valid = uniform(rows_valid);
+  lag = uniform(lag);
+  kb = uniform(kb);
+  const int slot = e / a.eps;
+  const int64_t grow0 = (int64_t)uniform(a.expert_off[e]) + row0;
+  const int nk = uniform(nkt);
+
+  const char *A = uniform(slot_addr(a, slot, g.a_win, (uint64_t)grow0 * g.lda * 2));
+  const char *B = uniform((const char *)(g.w + (int64_t)e * g.w_estride));
+  // operand byte ranges: the tile's receive rows, the expert's weights
+  const __amdgpu_buffer_rsrc_t ra =
+      byte_range_rsrc(A, (uint32_t)rows_valid * (uint32_t)g.lda * 2u);
+  const __amdgpu_buffer_rsrc_t rb = byte_range_rsrc(B, (uint32_t)g.w_bytes);
+
+  // byte offset (at k = 0) of the chunk each lane loads; rows past the
+  // expert's last row re-read that row, so the load count never varies
+  const int ld_row = lane / CPR;
+  const int ld_pchunk = lane % CPR;
+  uint32_t oa[LA], ob[LB];
+#pragma unroll
+  for (int q = 0; q < LA; ++q) {
+    const int row = (q * NW + wave) * RPI + ld_row;
+    const int rr = row < rows_valid ? row : rows_valid - 1;
+    oa[q] = (uint32_t)rr * (uint32_t)g.lda * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
+    asm volatile("" : "+v"(oa[q]));
+  }
+#pragma unroll
+  for (int q = 0; q < LB; ++q) {
+    const int row = (q * NW + wave) * RPI + ld_row;
+    uint32_t grow;
+    if (SWIGLU) {
+      // wavefront column block jb: pair jb / 2, gate (even) or up (odd)
+      const int wnb = row / TN, jb = (row % TN) / 32, sub = row % 32;
+      const int i = n_tile * (BN / 2) + wnb * (TN / 2) + (jb / 2) * 32 + sub;
+      grow = (jb & 1) ? (uint32_t)(g.up_off + i) : (uint32_t)i;
+    } else {
+      grow = (uint32_t)(n_tile * BN + row);
+    }
+    ob[q] = grow * (uint32_t)g.ldb * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
+    asm volatile("" : "+v"(ob[q]));
+  }
+  // LDS fragment addresses, per ring stage and MFMA sub-step.  The rows of
+  // one wavefront's blocks differ by multiples of 32, so they share the row
+  // swizzle and differ by constant offsets (folded into the instructions).
+  // Kept opaque so the compiler does not recompute them inside the loop.
+  uint32_t fa_addr[STAGES][KSUB], fb_addr[STAGES][KSUB];
+  {
+    const int l = lane & 31;
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st)
+#pragma unroll
+      for (int sk = 0; sk < KSUB; ++sk) {
+        const int c = sk * 2 + (lane >> 5);
+        const uint32_t lp = (uint32_t)(l * ROWB + ((c ^ swz<CPR>(l)) * 16));
+        fa_addr[st][sk] = base + st * STAGE_BYTES + wm * 32 * ROWB + lp;
+        fb_addr[st][sk] = base + st * STAGE_BYTES + A_BYTES + wn * TN * ROWB + lp;
+        asm volatile("" : "+v"(fa_addr[st][sk]), "+v"(fb_addr[st][sk]));
+      }
+  }
+
+  // load q (0 .. LPS-1: A loads, then B loads) of this wavefront's share of
+  // K-step kt (the tail re-loads the last one) into ring stage ST; K-steps
+  // run from kb + lag, wrapping inside [kb, kb + nk).  Scalar offsets only.
+  auto issue_load = [&](auto st_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value, q = decltype(q_c)::value;
+    char *sbase = smem + ST * STAGE_BYTES;
+    if constexpr (q < LA)
+      buffer_load_lds_16(ra, oa[q], soff, sbase + (q * NW + wave) * 1024);
+    else
+      buffer_load_lds_16(rb, ob[q - LA], soff, sbase + A_BYTES + ((q - LA) * NW + wave) * 1024);
+  };
+  auto k_offset = [&](int kt) __attribute__((always_inline)) {
+    int kc = (kt < nk ? kt : nk - 1) + lag;
+    if (kc >= nk) kc -= nk;
+    return (uint32_t)(kb + kc) * ROWB;
+  };
+
+  // this wavefront's blocks (wm + WM i) holding rows: a prefix i < nact
+  const int mblocks = (rows_valid + 31) / 32;
+  const int nact = min(FM, max(0, (mblocks - wm + WM - 1) / WM));
+  uint16_t *C = (uint16_t *)slot_addr(a, slot, g.c_win, (uint64_t)grow0 * g.ldc * 2);
+
+  // The whole tile for a wavefront with NACT active row blocks: the
+  // accumulators live only inside one specialisation.
+  auto k_loop = [&](auto nact_c) __attribute__((always_inline)) {
+    constexpr int NACT = decltype(nact_c)::value;
+    constexpr int NF = NACT > 0 ? NACT : 1;
+    f32x16 acc[NF][FN];
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    constexpr int NRD = NACT > 0 ? NACT + FN : 0;  // fragment reads per sub-step
+    constexpr int H0 = LPS / 2;                     // loads issued in sub-step 0
+    constexpr int H1 = LPS - H0;                    // ... and in sub-step 1
+    // fragments of the two sub-steps (double buffer: one is multiplied while
+    // the other is read).  Read order: the FN B fragments, then the NACT A
+    // fragments, so that row i of MFMAs can start once A fragment i is in.
+    bf16x8 fa[2][NF], fb[2][FN];
+    auto read_frag = [&](auto buf_c, auto st_c, auto sk_c, auto r_c) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(buf_c)::value, ST = decltype(st_c)::value;
+      constexpr int SK = decltype(sk_c)::value, r = decltype(r_c)::value;
+      if constexpr (r < FN)
+        fb[BUF][r] = *((lds_bf16x8_t *)(uintptr_t)fb_addr[ST][SK] + r * 32 * ROWB / 16);
+      else
+        fa[BUF][r - FN] =
+            *((lds_bf16x8_t *)(uintptr_t)fa_addr[ST][SK] + (r - FN) * WM * 32 * ROWB / 16);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // prologue: K-steps 0 .. STAGES-2 in flight; stage 0 complete
+    // everywhere; the fragments of (K-step 0, sub-step 0) read into buffer 0
+    static_for<STAGES - 1>([&](auto p_c) __attribute__((always_inline)) {
+      const uint32_t soff = k_offset(decltype(p_c)::value);
+      static_for<LPS>([&](auto q_c) __attribute__((always_inline)) { issue_load(p_c, q_c, soff); });
+    });
+    wait_vmcnt<(STAGES - 2) * LPS>();
+    stage_barrier();
+    static_for<NRD>([&](auto r_c) __attribute__((always_inline)) { read_frag(I0{}, I0{}, I0{}, r_c); });
+
+    // K-step kt, whose stage is ST = kt % STAGES.  Each wavefront issues, in
+    // order (one item after each MFMA):
+    //  sub-step 0: MFMAs of (kt, 0) from buffer 0; items: the reads of
+    //    (kt, 1) into buffer 1, then H0 loads of K-step kt+STAGES-1 (into
+    //    the slot K-step kt-1 used, free since the previous barrier);
+    //  sub-step 1: MFMAs of (kt, 1) from buffer 1; after the first row:
+    //    wait for its own reads of stage kt and its own share of stage kt+1,
+    //    barrier (stage kt+1 complete everywhere, stage kt's slot free from
+    //    the next K-step on); items: the reads of (kt+1, 0) into buffer 0,
+    //    then the other H1 loads.
+    // Before MFMA row i, a progressive lgkmcnt wait lets the row start as
+    // soon as its A fragment (and the B fragments read before it) are in.
+    auto step = [&](auto st_c, int kt) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr int NST = (ST + 1) % STAGES;            // stage of K-step kt+1
+      constexpr int LST = (ST + STAGES - 1) % STAGES;   // stage of K-step kt+STAGES-1
+      const uint32_t soff = k_offset(kt + STAGES - 1);
+      // ---- sub-step 0
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        // new reads issued before row i: one per earlier MFMA, at most NRD
+        constexpr int ISSUED = (i * FN < NRD) ? i * FN : NRD;
+        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value, m = i * FN + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], acc[i][j], 0, 0, 0);
+          if constexpr (m < NRD) read_frag(I1{}, st_c, I1{}, std::integral_constant<int, m>{});
+          else if constexpr (m - NRD < H0)
+            issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, m - NRD>{}, soff);
+        });
+      });
+      // items the MFMAs did not cover (few active rows)
+      constexpr int NMF = NACT * FN;
+      static_for<(NRD + H0 > NMF) ? NRD + H0 - NMF : 0>([&](auto t_c) __attribute__((always_inline)) {
+        constexpr int m = NMF + decltype(t_c)::value;
+        if constexpr (m < NRD) read_frag(I1{}, st_c, I1{}, std::integral_constant<int, m>{});
+        else issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, m - NRD>{}, soff);
+      });
+      // ---- sub-step 1
+      // The barrier of K-step kt: every wavefront's share of stage kt+1 has
+      // landed, and every wavefront's reads of stage kt are complete (the
+      // DMA that next refills stage kt's slot is issued after this barrier).
+      auto sync = [&]() __attribute__((always_inline)) {
+        wait_lgkmcnt<0>();                      // own reads of stage kt done
+        wait_vmcnt<(STAGES - 3) * LPS + H0>();  // own share of stage kt+1
+        stage_barrier();                        // ... for every wavefront
+      };
+      if constexpr (NACT == 0) sync();
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        // items start after row 0 (and the barrier)
+        constexpr int ISSUED = (i == 0) ? 0 : (((i - 1) * FN < NRD) ? (i - 1) * FN : NRD);
+        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value, m = (i - 1) * FN + j;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+          if constexpr (i >= 1) {
+            if constexpr (m < NRD) read_frag(I0{}, std::integral_constant<int, NST>{}, I0{}, std::integral_constant<int, m>{});
+            else if constexpr (m - NRD < H1)
+              issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, H0 + m - NRD>{}, soff);
+          }
+        });
+        if constexpr (i == 0) sync();
+      });
+      constexpr int NMF1 = NACT > 0 ? (NACT - 1) * FN : 0;
+      static_for<(NRD + H1 > NMF1) ? NRD + H1 - NMF1 : 0>([&](auto t_c) __attribute__((always_inline)) {
+        constexpr int m = NMF1 + decltype(t_c)::value;
+        if constexpr (m < NRD) read_frag(I0{}, std::integral_constant<int, NST>{}, I0{}, std::integral_constant<int, m>{});
+        else issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, H0 + m - NRD>{}, soff);
+      });
+    };
+    // K-steps in rounds of STAGES, so that each step's stage is a constant
+    int kt = 0;
+    for (; kt + STAGES <= nk; kt += STAGES)
+      static_for<STAGES>([&](auto p) __attribute__((always_inline)) {
+        step(p, kt + decltype(p)::value);
+      });
+    static_for<STAGES - 1>([&](auto p) __attribute__((always_inline)) {
+      if (kt + decltype(p)::value < nk) step(p, kt + decltype(p)::value);
+    });
+    wait_lgkmcnt<0>();
+    wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
+    // every wavefront is done with the LDS before the next tile refills it
+    __syncthreads();
+
+    if (part != nullptr) {
+      // partial sums of a K-range: straight from the accumulators, 32
+      // consecutive floats of two rows per store
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        const int rb = (wm + i * WM) * 32 + (lane / 32) * 4;
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          asm volatile("" : "+a"(acc[i][j]));
+          const int col = wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            part[(rb + (v / 4) * 8 + (v % 4)) * BN + col] = acc[i][j][v];
+        });
+      });
+      return;
+    }
+
+    // Epilogue, through the (now idle) ring: the wavefronts write the tile,
+    // rounded to bf16, row-major into LDS; then all threads copy the rows
+    // that exist to the staging window in 16-byte pieces.  Rows carry 16
+    // bytes of padding, so the two half-wavefronts of one LDS write (rows r
+    // and r + 4) land on different banks.
+    // In a 32x32 block, lane holds column (lane % 32), rows
+    // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v.  The
+    // empty asm statements pin each block's accumulator reads after the
+    // previous block's LDS writes, which keeps the compiler from hoisting
+    // every accumulator into VGPRs at once.
+    constexpr int OUT_COLS = SWIGLU ? BN / 2 : BN;
+    constexpr int OROWB = OUT_COLS * 2 + 16;
+    static_assert(BM * OROWB <= STAGES * STAGE_BYTES, "the output tile must fit the ring");
+    typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
+    lds_char_t *otile = (lds_char_t *)smem;
+    static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_c)::value;
+      const int rb = (wm + i * WM) * 32 + (lane / 32) * 4;
+      if constexpr (SWIGLU) {
+        static_for<FN / 2>([&](auto p_c) __attribute__((always_inline)) {
+          constexpr int p = decltype(p_c)::value;
+          asm volatile("" : "+a"(acc[i][2 * p]), "+a"(acc[i][2 * p + 1]));
+          const int col = wn * (TN / 2) + p * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rb + (v / 4) * 8 + (v % 4);
+            const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
+            *((lds_u16_t *)(otile + row * OROWB) + col) = f32_to_bf16_rne(h);
+          }
+        });
+      } else {
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          asm volatile("" : "+a"(acc[i][j]));
+          const int col = wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rb + (v / 4) * 8 + (v % 4);
+            *((lds_u16_t *)(otile + row * OROWB) + col) = f32_to_bf16_rne(acc[i][j][v]);
+          }
+        });
+      }
+    });
+    __syncthreads();
+    constexpr int CHUNKS = OUT_COLS * 2 / 16;  // 16-byte pieces per row
+    u32x4 *dst = (u32x4 *)(C + (int64_t)n_tile * OUT_COLS);
+    const int ldc16 = g.ldc / 8;
+    for (int idx = tid; idx < rows_valid * CHUNKS; idx += NW * kWave) {
+      const int row = idx / CHUNKS, ch = idx % CHUNKS;
+      dst[(int64_t)row * ldc16 + ch] = *((lds_u32x4_t *)(otile + row * OROWB) + ch);
+    }
+    __syncthreads();  // the ring is read out before the next tile refills it
+  };
+  // one specialisation per active-block count (wavefront-uniform branch)
+  static_for<FM + 1>([&](auto c) __attribute__((always_inline)) {
+    if (nact == decltype(c)::value) k_loop(c);
+  });
+}
+
+// Work list of one expert: its rows R = 256 q + r are covered by q full
+// 256-row m-tiles and, for r > 0, a remainder.  A remainder of more than 128
+// rows is one more 256-row m-tile; one of at most 128 rows is a 128-row tile
+// twice as wide (when the column tiles pair up), so a few leftover rows cost
+// half the work of a full tile instead of all of it.
+struct ExpertTiles {
+  int q;       // full 256-row m-tiles
+  int rem;     // rows of the remainder (0: none)
+  bool half;   // remainder as 128 x (2 BN) tiles
+  int units;   // tiles in the list
+};
+
+__device__ __forceinline__ ExpertTiles expert_tiles(int rows, int ntl) {
+  ExpertTiles t;
+  t.q = rows / kBM;
+  t.rem = rows - t.q * kBM;
+  t.half = t.rem > 0 && t.rem <= kBM / 2 && ntl % 2 == 0;
+  t.units = t.half ? (ntl / 2) * (2 * t.q + 1) : (t.q + (t.rem > 0)) * ntl;
+  return t;
+}
+
+// Tile r (0 <= r < units) of an expert with `rows` rows, in list order:
+// n-tile major, m-tile minor; with a half remainder, the column-tile pair
+// (2j, 2j+1) lists its full m-tiles and then the remainder tile j that spans
+// both (kind 2: 128 rows x 2 BN; kind 1: BM x BN).
+struct TileRef {
+  int kind, n_tile, m_tile, row0, rows_valid;
+};
+
+__device__ __forceinline__ TileRef decode_tile(const ExpertTiles &et, int r, int rows) {
+  TileRef t;
+  if (et.half && r % (2 * et.q + 1) == 2 * et.q) {
+    t.kind = 2;
+    t.n_tile = r / (2 * et.q + 1);
+    t.m_tile = et.q;
+    t.row0 = et.q * kBM;
+    t.rows_valid = et.rem;
+  } else {
+    if (et.half) {
+      const int per = 2 * et.q + 1;
+      const int j = r / per;
+      const int rr = r - j * per;
+      t.n_tile = 2 * j + rr / et.q;
+      t.m_tile = rr % et.q;
+    } else {
+      const int mt_e = et.q + (et.rem > 0);
+      t.n_tile = r / mt_e;
+      t.m_tile = r - t.n_tile * mt_e;
+    }
+    t.kind = 1;
+    t.row0 = t.m_tile * kBM;
+    t.rows_valid = min(kBM, rows - t.row0);
+  }
+  return t;
+}
+
+// Descriptors of the two expert GEMMs over the windows of `a` (the tile
+// queues and the split-tile state are the caller's to set).
+inline GemmDesc gemm_desc_gate_up(const MoeArgs &a, const uint16_t *w13) {
+  GemmDesc g{};
+  g.a_win = a.off_disp_x;
+  g.lda = a.H;
+  g.w = w13;
+  g.w_estride = (int64_t)2 * a.I * a.H;
+  g.w_bytes = g.w_estride * 2;
+  g.ldb = a.H;
+  g.c_win = a.off_hbuf;
+  g.ldc = a.I;
+  g.kdim = a.H;
+  g.ntiles = a.I / (kBN / 2);
+  g.up_off = a.I;
+  return g;
+}
+
+inline GemmDesc gemm_desc_down(const MoeArgs &a, const uint16_t *w2) {
+  GemmDesc g{};
+  g.a_win = a.off_hbuf;
+  g.lda = a.I;
+  g.w = w2;
+  g.w_estride = (int64_t)a.H * a.I;
+  g.w_bytes = g.w_estride * 2;
+  g.ldb = a.I;
+  g.c_win = a.off_out;
+  g.ldc = a.H;
+  g.kdim = a.I;
+  g.ntiles = a.H / kBN;
+  g.up_off = 0;
+  return g;
+}
+
+// Tiles of one expert's GEMM that cover its m-tile m (rows [256 m, 256 m +
+// 256)): every column tile, or every pair of them for a half remainder.
+__device__ __forceinline__ int tiles_per_mtile(const ExpertTiles &et, int m, int ntl) {
+  return (et.half && m == et.q) ? ntl / 2 : ntl;
+}
+
+}  // namespace
+}  // namespace cco

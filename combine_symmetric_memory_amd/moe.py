@@ -255,6 +255,27 @@ class MoE:
         check(code, "cco_moe_combine", allow=(_capi.CCO_OK, _capi.CCO_INFO_COPIED))
         return out, code
 
+    def fused(self, idx: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
+              w13: torch.Tensor | None, w2: torch.Tensor | None,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """cco_moe_fused: the whole path in one launch; returns out bf16 [T, H]."""
+        T = idx.shape[0]
+        if idx.dim() != 2 or idx.shape[1] != self.K or tuple(x.shape) != (T, self.H) or \
+           tuple(w.shape) != (T, self.K):
+            raise ValueError("idx [T, K], x [T, H] and w [T, K] expected")
+        if self.I > 0 and (tuple(w13.shape) != (self.E, 2 * self.I, self.H) or
+                           tuple(w2.shape) != (self.E, self.H, self.I)):
+            raise ValueError("w13 must be [E, 2I, H] and w2 [E, H, I]")
+        if out is None:
+            out = torch.empty((T, self.H), dtype=torch.bfloat16, device=x.device)
+        check(lib.cco_moe_fused(self.handle, _ptr(idx, torch.int32, "idx"),
+                                _ptr(x, torch.bfloat16, "x"), _ptr(w, torch.float32, "w"),
+                                _ptr(w13, torch.bfloat16, "w13"), _ptr(w2, torch.bfloat16, "w2"),
+                                _ptr(out, torch.bfloat16, "out"), T, _stream(stream)),
+              "cco_moe_fused")
+        self.T = T
+        return out
+
     def stage_in_sdma(self, slot: int, src: torch.Tensor | int, rows: int, stream=None) -> None:
         """cco_moe_stage_in_sdma: rows of `src` (bf16 [rows, H] tensor or a
         device address) into slot's staging window on the copy engines."""

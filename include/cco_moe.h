@@ -59,7 +59,9 @@ typedef enum {
   CCO_ERR_CAPACITY = -4,       /* device: a slot received more than cap rows */
   CCO_ERR_BAD_EXPERT = -5,     /* device: an expert id outside [0, E) */
   CCO_ERR_HEAP_FULL = -6,      /* the heap's slots have no room for this object */
-  CCO_ERR_TOO_LARGE = -7       /* the batch exceeds the fixed scratch of cco_moe_plan_noalloc */
+  CCO_ERR_TOO_LARGE = -7,      /* the batch exceeds the fixed scratch of cco_moe_plan_noalloc */
+  CCO_ERR_TIMEOUT = -8,        /* device: a wait of cco_moe_fused gave up; outputs undefined */
+  CCO_ERR_DISABLED = -9        /* the entry point is switched off in this build */
 } cco_status;
 
 /* Opaque handles. */
@@ -259,6 +261,37 @@ void *cco_moe_combine_in_view(cco_moe *m, int32_t slot);
 int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weights,
                     uint16_t *out, int32_t T, void *stream);
 
+/* SWITCHED OFF in this build: returns CCO_ERR_DISABLED before any launch
+ * (its kernel faulted the GPU on its first run and the cause is not yet
+ * shown).  The contract below is the one it is built to.
+ *
+ * The whole path -- plan, dispatch, expert (SwiGLU gate/up and down),
+ * combine -- in ONE persistent kernel launch ([blog] "Mega-MoE: mega-kernel
+ * co-design with FlyDSL": dispatch, expert GEMM and combine fused into one
+ * kernel with no synchronisation between kernels; "In-kernel
+ * compute-communication fusion": the stages overlap at tile granularity).
+ * Arguments as for cco_moe_plan, cco_moe_dispatch, cco_moe_expert and
+ * cco_moe_combine with expert_out = NULL, in that order, and it leaves the
+ * object in the same state: routing state, receive, intermediate and
+ * staging windows, and `out`.  Plan, dispatch and combine (of the same expert
+ * rows) are bit-identical to the separate calls; the expert tiles are the
+ * same, except that this path never sums a tile in K-ranges (the separate
+ * GEMMs do for the last tiles of a GEMM with few rounds), so those tiles may
+ * differ by rounding.
+ * Inside the launch a down tile starts once the gate/up tiles of its rows
+ * are done, and a block of tokens is combined once the down tiles of its
+ * rows are; expert tiles start once their expert's rows have arrived.  The
+ * waits are bounded: if the grid cannot make progress (for example when
+ * other work holds some of the compute units), the status word becomes
+ * CCO_ERR_TIMEOUT after about two seconds and the kernel exits.
+ * Errors: CCO_ERR_INVALID_ARG (as the separate calls, and for top-k above
+ * 8), CCO_ERR_HIP; device
+ * errors as cco_moe_plan, plus CCO_ERR_TIMEOUT (all read by cco_moe_status).
+ */
+int cco_moe_fused(cco_moe *m, const int32_t *topk_idx, const uint16_t *x, const float *weights,
+                  const uint16_t *w13, const uint16_t *w2, uint16_t *out, int32_t T,
+                  void *stream);
+
 /* Copy one slot's expert output from a buffer of the caller's into that
  * slot's combine staging window on the GPU's copy engines (SDMA), not on
  * compute units ([blog] "Multiple communication transports": SDMA serves
@@ -325,9 +358,10 @@ int cco_moe_plan_noalloc(const int32_t *topk_idx, int32_t T, int32_t K, int32_t 
  * total milliseconds (kinds: 0 plan-count (the whole plan for a batch of
  * at most 2048 (token, k) pairs, which runs in one launch), 1 plan-rank, 2 dispatch,
  * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in,
- * 7 8-bit dispatch, 8 staging copy on the copy engines).
+ * 7 8-bit dispatch, 8 staging copy on the copy engines, 9 the single-launch
+ * path of cco_moe_fused).
  * Reading the summary synchronises the recorded events and resets it. */
-#define CCO_NUM_KERNEL_KINDS 9
+#define CCO_NUM_KERNEL_KINDS 10
 int cco_moe_set_timing(cco_moe *m, int enable);
 int cco_moe_timing_summary(cco_moe *m, int32_t *launches, double *total_ms);
 

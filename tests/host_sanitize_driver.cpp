@@ -42,6 +42,11 @@ hipError_t launch_expert_gate_up(const MoeArgs &, const uint16_t *, int32_t, int
 hipError_t launch_expert_down(const MoeArgs &, const uint16_t *, int32_t, int, hipStream_t) {
   return hipErrorInvalidValue;
 }
+hipError_t launch_fused(const MoeArgs &, const FusedBuffers &, const int32_t *, const uint16_t *,
+                        const float *, const uint16_t *, const uint16_t *, uint16_t *, int32_t,
+                        int, hipStream_t) {
+  return hipErrorInvalidValue;
+}
 }  // namespace cco
 
 #define CHECK(c)                                                        \
@@ -63,7 +68,7 @@ static cco_moe_shape shape(int T, int H, int K, int E, int I) {
 }
 
 int main() {
-  for (int c = -9; c <= 2; ++c) CHECK(cco_status_string(c) != nullptr);
+  for (int c = -11; c <= 2; ++c) CHECK(cco_status_string(c) != nullptr);
 
   // valid shapes: the windows are ordered, aligned and sized as declared
   const cco_moe_shape ok[] = {shape(128, 256, 2, 8, 512), shape(8192, 7168, 8, 256, 2048),
@@ -140,6 +145,8 @@ int main() {
   CHECK(cco_moe_combine(nullptr, nullptr, nullptr, nullptr, 0, nullptr) == CCO_ERR_INVALID_ARG);
   CHECK(cco_moe_status(nullptr, nullptr, nullptr, nullptr) == CCO_ERR_INVALID_ARG);
   CHECK(cco_moe_stage_in_sdma(nullptr, 0, nullptr, 0, nullptr) == CCO_ERR_INVALID_ARG);
+  CHECK(cco_moe_fused(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) ==
+        CCO_ERR_INVALID_ARG);
   CHECK(cco_moe_dispatch_view(nullptr, 0) == nullptr);
   CHECK(cco_moe_combine_in_view(nullptr, 0) == nullptr);
   CHECK(cco_moe_set_timing(nullptr, 1) == CCO_ERR_INVALID_ARG);

@@ -220,3 +220,34 @@ def test_mixtral_full(orc):
     tokens = np.array([0, 1, 2047, cfg.T - 1])
     _end_to_end_tokens(orc, c, tokens, got[tokens])
     heap.destroy()
+
+
+@pytest.mark.skip(reason="cco_moe_fused is switched off: its kernel faulted the GPU on its "
+                         "first run (the small config) and the cause is not yet shown")
+@pytest.mark.parametrize("name", ["dsv3", "decode", "mixtral"])
+def test_fused_full(orc, name):
+    """The single-launch path at full size: plan and dispatch bit-exact,
+    the first and last row of every expert within tolerance, combine of every
+    token bit-exact on the GPU's own expert rows; against the separate
+    launches, identical where they sum no tile in K-ranges (dsv3, decode) and
+    within tolerance where they do (mixtral's down projection)."""
+    import combine_symmetric_memory_amd as ccm
+    cfg = get_config(name)
+    say("case: fused full size", cfg)
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    sep, code = run_path(moe, c)
+    assert code == 0
+    sep = bf16_bits(sep)
+    out = moe.fused(c.idx, c.x, c.w, c.w13, c.w2)
+    torch.cuda.synchronize()
+    code, _, _ = moe.status()
+    assert code == ccm.CCO_OK, ccm.status_string(code)
+    ref = _plan_and_dispatch_exact(orc, moe, c)
+    _rows_parity(orc, moe, c, ref, _first_last_rows(ref.counts), "fused: first and last rows")
+    got = _combine_all_tokens_exact(orc, moe, c, ref, out)
+    if name == "mixtral":
+        assert_close(got, sep, "fused vs separate launches")
+    else:
+        np.testing.assert_array_equal(got, sep)
+    heap.destroy()

@@ -468,3 +468,19 @@ def test_stage_in_on_the_copy_engines(ccm):
     assert lib.cco_moe_stage_in_sdma(h, 0, view, 64, None) == ccm.CCO_OK     # the view itself
     torch.cuda.synchronize()
     heap.destroy()
+
+
+def test_fused_entry_point_reports_it_is_switched_off(ccm):
+    # the single-launch path is not built in this library (its kernel faulted
+    # the GPU on its first run, cause not yet shown): the call must say so
+    # before launching anything
+    cfg = get_config("tiny")
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    from combine_symmetric_memory_amd import _capi
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    rc = _capi.lib.cco_moe_fused(moe.handle, c.idx.data_ptr(), c.x.data_ptr(), c.w.data_ptr(),
+                                 c.w13.data_ptr(), c.w2.data_ptr(), out.data_ptr(), cfg.T, None)
+    assert rc == ccm.CCO_ERR_DISABLED
+    assert ccm.status_string(rc) == "CCO_ERR_DISABLED"
+    heap.destroy()
