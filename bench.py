@@ -88,48 +88,59 @@ def code_digest(path):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
+EXPERT_SOURCES = ("expert.hip", "gemm_tile.h")
+
+
+def expert_digest():
+    """Digest of the expert GEMM's code (the kernel file and its tile)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "combine_symmetric_memory_amd", "csrc")
+    parts = [code_digest(os.path.join(csrc, f)) for f in EXPERT_SOURCES]
+    return hashlib.sha256("".join(parts).encode()).hexdigest()
+
+
 def profiled_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None if there is none for this workload or the expert kernel's
     code changed since the counters were taken."""
     import re
     path = os.path.join(ROOT, "profiles", "traffic_%s.md" % workload)
-    src = os.path.join(ROOT, "combine_symmetric_memory_amd", "csrc", "expert.hip")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"expert_code_sha256: ([0-9a-f]+)", text)
-    if not m or m.group(1) != code_digest(src):
+    if not m or m.group(1) != expert_digest():
         return None
     m = re.search(r"traffic_bytes_per_launch %s: (\d+)" % re.escape(kernel), text)
     return int(m.group(1)) if m else None
 
 
 def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthreads):
-    """The oracle, untuned, on a bounded sample of the same workload; returns
-    a dict in tokens/s."""
+    """The oracle, untuned, timed on the host: plan, dispatch and combine on
+    the full batch (each the median of 3 runs; the oracle runs them on one
+    thread), the SwiGLU expert on every row of a stratified set of experts
+    (the smallest, the median and the largest) with `nthreads` threads,
+    extrapolated to all T * K rows by rows per second.  Returns tokens/s."""
     import numpy as np
 
     from oracle import oracle as orc
 
-    eps = cfg.eps
-    t0 = time.perf_counter()
-    pl = orc.plan(idx_np, cfg.E, cfg.S, cfg.cap)
-    t_plan = time.perf_counter() - t0
-    # dispatch and combine on a token sample (the oracle writes full slot
-    # arrays, so its dispatch runs on a sub-batch sized for them)
-    ts = min(cfg.T, 256)
-    sub_idx, sub_w, sub_x = idx_np[:ts], w_np[:ts], x_np[:ts]
-    sub_cap = ts * min(cfg.K, eps)
-    sp = orc.plan(sub_idx, cfg.E, cfg.S, sub_cap)
-    t0 = time.perf_counter()
-    d = orc.dispatch(sub_x, sub_w, sub_idx, sp.pos, cfg.E, cfg.S, sub_cap)
-    t_disp = (time.perf_counter() - t0) / ts
-    t0 = time.perf_counter()
-    orc.combine_tokens(d.disp_x, sub_w, sub_idx, sp.pos, cfg.E, cfg.S)
-    t_comb = (time.perf_counter() - t0) / ts
+    def median3(fn):
+        times, out = [], None
+        for _ in range(3):
+            out = None
+            t0 = time.perf_counter()
+            out = fn()
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), out
+
+    E, S, cap = cfg.E, cfg.S, cfg.cap
+    t_plan, pl = median3(lambda: orc.plan(idx_np, E, S, cap))
+    t_disp, d = median3(lambda: orc.dispatch(x_np, w_np, idx_np, pl.pos, E, S, cap))
+    # combine over the receive rows: the same rows, weights and arithmetic as
+    # over expert outputs (identity experts read exactly these)
+    t_comb, _ = median3(lambda: orc.combine_tokens(d.disp_x, w_np, idx_np, pl.pos, E, S))
     del d
-    # expert: every row of the sampled experts
     rows = 0
     t_exp = 0.0
     if cfg.I > 0:
@@ -141,15 +152,17 @@ def cpu_baseline(cfg, x_np, idx_np, w_np, w13_host, sample_experts, counts, nthr
             t_exp += time.perf_counter() - t0
             rows += X.shape[0]
     per_row = t_exp / rows if rows else 0.0
-    step_s = t_plan + cfg.T * (t_disp + t_comb) + cfg.T * cfg.K * per_row
-    sample = ("plan on all %d (token, k) pairs; dispatch and combine on %d tokens; "
-              "SwiGLU expert on all %d rows of experts %s with %d threads; step time "
-              "extrapolated to %d tokens x %d rows each" %
-              (cfg.T * cfg.K, ts, rows, list(sample_experts), nthreads, cfg.T, cfg.K))
+    TK = cfg.T * cfg.K
+    step_s = t_plan + t_disp + t_comb + TK * per_row
+    sample = ("full size, median of 3: plan, dispatch and combine of all %d tokens (%d pairs), "
+              "one thread each; SwiGLU expert on every row of the smallest, median and largest "
+              "experts %s (%d rows) with %d threads, extrapolated to all %d rows" %
+              (cfg.T, TK, list(sample_experts), rows, nthreads, TK))
     return {"value": round(cfg.T / step_s, 3), "unit": "tokens/s", "cores": int(nthreads),
             "kind": "oracle", "sample": sample,
-            "stage_s": {"plan": round(t_plan, 4), "dispatch_per_token": t_disp,
-                        "combine_per_token": t_comb, "expert_per_row": per_row}}
+            "stage_s": {"plan": round(t_plan, 4), "dispatch": round(t_disp, 4),
+                        "combine": round(t_comb, 4), "expert_per_row": per_row,
+                        "expert_extrapolated": round(TK * per_row, 3)}}
 
 
 def calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert=None):
@@ -557,9 +570,8 @@ def main():
         if cfg.I > 0:
             nz = np.nonzero(counts)[0]
             order = nz[np.argsort(counts[nz], kind="stable")]
-            # two experts near the median row count
-            mid = len(order) // 2
-            sample_experts = [int(order[mid]), int(order[mid + 1])]
+            # stratified: the smallest, the median and the largest expert
+            sample_experts = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
             w13_host = [(bf16_bits(w13[e]), bf16_bits(w2[e])) for e in sample_experts]
         from oracle import oracle as orc
         nthreads = orc.default_threads()

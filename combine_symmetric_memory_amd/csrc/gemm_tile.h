@@ -147,10 +147,21 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Full tile 256 x 256 x 32 with a 5-deep ring (32 KiB stages); the 128 x 512
-// remainder tile (40 KiB stages) with 4.  Either ring fills the 160 KiB of
-// LDS, so the kernel keeps nothing else there.
-constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 5, kStagesHalf = 4;
+// K-step of the expert GEMMs' main loop: 64 (rows read 128 bytes at a
+// time) by default, or 32 (64 bytes at a time, twice the L1 -> L2 requests
+// of the same bytes; about 1% slower on the DeepSeek-V3 shapes).  Both
+// divide every K the boundary accepts (H a multiple of 256, I of 128).
+#ifndef CCO_GEMM_BK
+#define CCO_GEMM_BK 64
+#endif
+// Full tile 256 x 256 and the 128 x 512 remainder tile.  With K-steps of
+// 32: a 5-deep ring of 32 KiB stages, and a 4-deep one of 40 KiB; with
+// K-steps of 64: two stages of 64 KiB, and two of 80 KiB.  Every ring fits
+// the 160 KiB of LDS, which the kernel keeps for it alone.
+constexpr int kBM = 256, kBN = 256, kBK = CCO_GEMM_BK;
+static_assert(kBK == 32 || kBK == 64, "K-step of 32 or 64");
+constexpr int kStages = kBK == 64 ? 2 : 5, kStagesHalf = kBK == 64 ? 2 : 4;
+constexpr int kGemmLdsBytes = 160 * 1024;
 
 // Wavefronts per workgroup: one per SIMD.
 constexpr int kGemmWaves = 4;
@@ -189,6 +200,17 @@ static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTi
 // two sub-steps, makes the next stage visible to every wavefront and frees
 // the ring slot of the previous one.
 //
+// BK = 64 (two stages, four sub-steps): one wavefront load covers 128
+// contiguous bytes of 8 rows instead of 64 bytes of 16, so a K-step's bytes
+// take half the L1 -> L2 requests.  K-step kt reads stage kt % 2.  The one
+// barrier per K-step sits in sub-step 3, after its first row of MFMAs: every
+// wavefront has then read its last fragments of stage kt and has its share
+// of stage kt+1 in LDS, so stage kt+1 is complete and stage kt's slot is
+// free.  Right after it the wavefront reads the fragments of (kt+1, 0) and
+// starts the loads of stage kt+2 into the freed slot, which go on through
+// sub-steps 0 and 1 of K-step kt+1; they have landed by the barrier of
+// K-step kt+1.
+//
 // n_tile counts BN-wide column tiles (for gate/up: BN/2 intermediate
 // columns, gate and up interleaved in 32-row blocks); rows [row0, row0 +
 // rows_valid) of expert e are computed over the nkt K-steps from kb on.
@@ -196,11 +218,10 @@ static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTi
 // otherwise the fp32 sums of this K-range are written to part, row-major
 // [BM][BN] in the accumulators' column order.  Every wavefront of the
 // workgroup calls this with the same arguments.
-template <int BM, int BN, int STAGES, bool SWIGLU>
+template <int BM, int BN, int STAGES, bool SWIGLU, int BK = kBK>
 __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
                                          int n_tile, int row0, int rows_valid, int lag, int kb,
                                          int nkt, float *part) {
-  constexpr int BK = kBK;
   constexpr int NW = kGemmWaves;
   constexpr int WM = BM / 128;          // wavefront rows
   constexpr int WN = NW / WM;           // wavefront columns
@@ -218,10 +239,12 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   constexpr int LPS = LA + LB;
   constexpr int KSUB = BK / 16;         // MFMA sub-steps per K-step
   static_assert(WM * WN == NW && FM == 4 && FN == 4, "4 x 4 blocks of 32 x 32 per wavefront");
-  static_assert(KSUB == 2, "a K-step is two MFMA sub-steps");
+  static_assert((KSUB == 2 && STAGES >= 3 && (STAGES - 2) * LPS < 64) ||
+                    (KSUB == 4 && STAGES == 2 && LPS < 64),
+                "K-steps of 32 with 3 or more stages, or of 64 with two");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
   static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
-  static_assert(STAGES >= 3 && (STAGES - 2) * LPS < 64, "stage count / vmcnt range");
+  static_assert(STAGES * STAGE_BYTES <= kGemmLdsBytes, "the ring must fit the LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -357,6 +380,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     stage_barrier();
     static_for<NRD>([&](auto r_c) __attribute__((always_inline)) { read_frag(I0{}, I0{}, I0{}, r_c); });
 
+    if constexpr (KSUB == 2) {
     // K-step kt, whose stage is ST = kt % STAGES.  Each wavefront issues, in
     // order (one item after each MFMA):
     //  sub-step 0: MFMAs of (kt, 0) from buffer 0; items: the reads of
@@ -437,6 +461,92 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     static_for<STAGES - 1>([&](auto p) __attribute__((always_inline)) {
       if (kt + decltype(p)::value < nk) step(p, kt + decltype(p)::value);
     });
+    } else {
+    // K-steps of 64: sub-steps 0..3 of K-step kt multiply fragment buffers
+    // 0, 1, 0, 1 and, one item after each MFMA, read the next sub-step's
+    // fragments into the other buffer and issue loads: [L3, L3 + L0) of
+    // stage kt+1 in sub-step 0, the rest in sub-step 1; in sub-step 3, after
+    // its first row and the barrier, the fragments of (kt+1, 0) and loads
+    // [0, L3) of stage kt+2 into the slot stage kt used.
+    constexpr int L3 = LPS / 4, L0 = LPS / 2, L1 = LPS - L3 - L0;
+    auto substep = [&](auto bufm_c, auto rbuf_c, auto rst_c, auto rsk_c, auto lst_c, auto q0_c,
+                       auto nq_c, uint32_t soff, auto sync_c) __attribute__((always_inline)) {
+      constexpr int BUFM = decltype(bufm_c)::value;  // buffer the MFMAs read
+      constexpr int RBUF = decltype(rbuf_c)::value;  // reads: into buffer RBUF,
+      constexpr int RST = decltype(rst_c)::value;    //   of stage slot RST,
+      constexpr int RSK = decltype(rsk_c)::value;    //   sub-step RSK
+      constexpr int LST = decltype(lst_c)::value;    // loads: into slot LST,
+      constexpr int Q0 = decltype(q0_c)::value;      //   loads Q0 ..
+      constexpr int NQ = decltype(nq_c)::value;      //   .. Q0 + NQ - 1
+      constexpr bool SYNC = decltype(sync_c)::value;
+      constexpr int NIT = NRD + NQ;
+      auto item = [&](auto m_c) __attribute__((always_inline)) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m < NRD)
+          read_frag(std::integral_constant<int, RBUF>{}, std::integral_constant<int, RST>{},
+                    std::integral_constant<int, RSK>{}, std::integral_constant<int, m>{});
+        else
+          issue_load(std::integral_constant<int, LST>{},
+                     std::integral_constant<int, Q0 + m - NRD>{}, soff);
+      };
+      // the barrier of the K-step: this wavefront's reads of the current
+      // stage and its loads of the next one are done, then every
+      // wavefront's
+      auto sync = [&]() __attribute__((always_inline)) {
+        wait_lgkmcnt<0>();
+        wait_vmcnt<0>();
+        stage_barrier();
+      };
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        // items start after row 0 in the sub-step with the barrier
+        constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
+        constexpr int ISSUED = BEFORE < NRD ? BEFORE : NRD;
+        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUFM][i], fb[BUFM][j], acc[i][j],
+                                                              0, 0, 0);
+          if constexpr (!(SYNC && i == 0)) {
+            constexpr int m = BEFORE + j;
+            if constexpr (m < NIT) item(std::integral_constant<int, m>{});
+          }
+        });
+        if constexpr (SYNC && i == 0) sync();
+      });
+      if constexpr (SYNC && NACT == 0) sync();
+      // items the MFMAs did not cover (few active rows)
+      constexpr int COVERED = NACT == 0 ? 0 : (SYNC ? (NACT - 1) * FN : NACT * FN);
+      static_for<(NIT > COVERED) ? NIT - COVERED : 0>([&](auto t_c) __attribute__((always_inline)) {
+        item(std::integral_constant<int, COVERED + decltype(t_c)::value>{});
+      });
+    };
+    using IT = std::true_type;
+    using IF = std::false_type;
+    auto step = [&](auto st_c, int kt) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;  // stage of K-step kt
+      constexpr int NS = 1 - ST;                 // stage of K-steps kt-1 and kt+1
+      using S = std::integral_constant<int, ST>;
+      using N = std::integral_constant<int, NS>;
+      const uint32_t s1 = k_offset(kt + 1), s2 = k_offset(kt + 2);
+      substep(I0{}, I1{}, S{}, I1{}, N{}, std::integral_constant<int, L3>{},
+              std::integral_constant<int, L0>{}, s1, IF{});
+      substep(I1{}, I0{}, S{}, std::integral_constant<int, 2>{}, N{},
+              std::integral_constant<int, L3 + L0>{}, std::integral_constant<int, L1>{}, s1, IF{});
+      substep(I0{}, I1{}, S{}, std::integral_constant<int, 3>{}, N{}, I0{}, I0{}, s1, IF{});
+      substep(I1{}, I0{}, N{}, I0{}, S{}, I0{}, std::integral_constant<int, L3>{}, s2, IT{});
+    };
+    // the first loads of stage 1 (those sub-step 3 of the step before issues)
+    static_for<L3>([&](auto q_c) __attribute__((always_inline)) {
+      issue_load(I1{}, q_c, k_offset(1));
+    });
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      step(I0{}, kt);
+      step(I1{}, kt + 1);
+    }
+    if (kt < nk) step(I0{}, kt);
+    }
     wait_lgkmcnt<0>();
     wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
     // every wavefront is done with the LDS before the next tile refills it
@@ -472,7 +582,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     // every accumulator into VGPRs at once.
     constexpr int OUT_COLS = SWIGLU ? BN / 2 : BN;
     constexpr int OROWB = OUT_COLS * 2 + 16;
-    static_assert(BM * OROWB <= STAGES * STAGE_BYTES, "the output tile must fit the ring");
+    static_assert(BM * OROWB <= kGemmLdsBytes, "the output tile must fit the LDS");
     typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
     typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
     lds_char_t *otile = (lds_char_t *)smem;
