@@ -252,10 +252,11 @@ def calibrate(cfg, moe, w, out, work, stream, dev, torch, per_expert=None):
 def stage_in_variant(cfg, moe, slot_total, stream, dev, torch):
     """The expert output of every slot handed over in buffers of the
     caller's and staged into the combine windows on the copy engines
-    (cco_moe_stage_in_sdma, no kernel), against the same bytes moved by the
-    library's copy kernel on the compute units (the copy fallback inside
-    cco_moe_combine); then each beside a large vendor GEMM on another stream,
-    to show what the copy takes from the compute units."""
+    (cco_moe_stage_in_sdma, no kernel), against the same bytes moved by a
+    copy kernel on the compute units (torch's device-to-device copy; the
+    library's own copy fallback runs at about the same rate); then each beside
+    a large vendor GEMM on another stream, to show what the copy takes from
+    the compute units."""
     import numpy as np
     flush = CacheFlush(torch, dev)
     rows = [int(r) for r in slot_total]
@@ -269,8 +270,7 @@ def stage_in_variant(cfg, moe, slot_total, stream, dev, torch):
         for s in range(cfg.S):
             moe.stage_in_sdma(s, foreign[s], rows[s], stream=st)
 
-    # the copy kernel of the fallback, on the same bytes (its per-launch
-    # times from the library's own events)
+    # a copy kernel on the compute units, on the same bytes
     dst = [torch.empty_like(f) for f in foreign]
 
     def cu_copy(st):

@@ -168,16 +168,11 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
         d[6] = xcd * W + v;  // workspace slot of the first range
       }
     }
-    // Tiles sharing a weight panel or receive rows run side by side on one
-    // XCD; rotating the K order by a small tile-dependent lag keeps them from
-    // missing the same L2 lines at the same moment.
-    const int lag = (n_tile % 8 + m_tile % 4) % nkt;
     if (kind == 2)
       run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid,
-                                                      lag, kb, nkt, part);
+                                                      kb, nkt, part);
     else
-      run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid, lag, kb, nkt,
-                                          part);
+      run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid, kb, nkt, part);
   }
   // the last workgroup out has seen every counter exhausted: rearm them for
   // the next launch (ordered by the stream)
@@ -265,8 +260,8 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(MoeArgs a, GemmDesc g)
 }
 
 constexpr size_t kGemmLds =
-    std::max((size_t)kStages * (kBM + kBN) * kBK * 2,
-             (size_t)kStagesHalf * (kBM / 2 + 2 * kBN) * kBK * 2);
+    std::max((size_t)ring_bytes(kBM, kBN, kStages, kBK),
+             (size_t)ring_bytes(kBM / 2, 2 * kBN, kStagesHalf, kBK));
 
 // The tail and fixup launches follow only when the GEMM may split, that is
 // when it can have fewer than kSplitMaxRounds rounds: every expert's rows R
@@ -316,3 +311,5 @@ hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int32_t T, i
 }
 
 }  // namespace cco
+
+

@@ -260,13 +260,12 @@ __device__ __forceinline__ void fused_tile(const MoeArgs &a, const FusedArgs &f,
     acquire_geq(f.q, a.status, f.gu_done + mt, tiles_per_mtile(eg, t.m_tile, f.gu.ntiles));
   }
   const int nk = g.kdim / kBK;
-  const int lag = (t.n_tile % 8 + t.m_tile % 4) % nk;
   if (t.kind == 2)
     run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU>(a, g, smem, e, t.n_tile, t.row0,
-                                                    t.rows_valid, lag, 0, nk, nullptr);
+                                                    t.rows_valid, 0, nk, nullptr);
   else
-    run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, t.n_tile, t.row0, t.rows_valid, lag, 0,
-                                        nk, nullptr);
+    run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, t.n_tile, t.row0, t.rows_valid, 0, nk,
+                                        nullptr);
   release_add((SWIGLU ? f.gu_done : f.dn_done) + mt, 1);
 }
 
@@ -396,8 +395,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(MoeArgs a, FusedAr
 }
 
 constexpr size_t kFusedLds =
-    std::max((size_t)kStages * (kBM + kBN) * kBK * 2,
-             (size_t)kStagesHalf * (kBM / 2 + 2 * kBN) * kBK * 2);
+    std::max((size_t)ring_bytes(kBM, kBN, kStages, kBK),
+             (size_t)ring_bytes(kBM / 2, 2 * kBN, kStagesHalf, kBK));
 static_assert(kFusedLds >= (size_t)(7 * 1056 + 8) * 4, "the plan, the tables and the broadcast words fit");
 
 template <int KT, int NVL, int GV>

@@ -155,13 +155,21 @@ __device__ __forceinline__ void static_for(F &&f) {
 #define CCO_GEMM_BK 64
 #endif
 // Full tile 256 x 256 and the 128 x 512 remainder tile.  With K-steps of
-// 32: a 5-deep ring of 32 KiB stages, and a 4-deep one of 40 KiB; with
-// K-steps of 64: two stages of 64 KiB, and two of 80 KiB.  Every ring fits
-// the 160 KiB of LDS, which the kernel keeps for it alone.
+// 32: a 5-deep ring of 32 KiB stages, and a 4-deep one of 40 KiB.  With
+// K-steps of 64 the full tile keeps its operands in rings of their own, two
+// 32 KiB slots of A and three of B (STAGES == 5 names that layout), and the
+// remainder tile two stages of 80 KiB.  Every ring fits the 160 KiB of LDS,
+// which the kernel keeps for it alone.
 constexpr int kBM = 256, kBN = 256, kBK = CCO_GEMM_BK;
 static_assert(kBK == 32 || kBK == 64, "K-step of 32 or 64");
-constexpr int kStages = kBK == 64 ? 2 : 5, kStagesHalf = kBK == 64 ? 2 : 4;
+constexpr int kStages = 5, kStagesHalf = kBK == 64 ? 2 : 4;
 constexpr int kGemmLdsBytes = 160 * 1024;
+
+// LDS bytes of a tile's ring (STAGES == 5 with K-steps of 64: two A slots
+// and three B slots)
+constexpr int ring_bytes(int bm, int bn, int stages, int bk) {
+  return (bk == 64 && stages == 5) ? (2 * bm + 3 * bn) * bk * 2 : stages * (bm + bn) * bk * 2;
+}
 
 // Wavefronts per workgroup: one per SIMD.
 constexpr int kGemmWaves = 4;
@@ -200,16 +208,22 @@ static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTi
 // two sub-steps, makes the next stage visible to every wavefront and frees
 // the ring slot of the previous one.
 //
-// BK = 64 (two stages, four sub-steps): one wavefront load covers 128
-// contiguous bytes of 8 rows instead of 64 bytes of 16, so a K-step's bytes
-// take half the L1 -> L2 requests.  K-step kt reads stage kt % 2.  The one
-// barrier per K-step sits in sub-step 3, after its first row of MFMAs: every
-// wavefront has then read its last fragments of stage kt and has its share
-// of stage kt+1 in LDS, so stage kt+1 is complete and stage kt's slot is
-// free.  Right after it the wavefront reads the fragments of (kt+1, 0) and
-// starts the loads of stage kt+2 into the freed slot, which go on through
-// sub-steps 0 and 1 of K-step kt+1; they have landed by the barrier of
-// K-step kt+1.
+// BK = 64 (four sub-steps): one wavefront load covers 128 contiguous bytes
+// of 8 rows instead of 64 bytes of 16, so a K-step's bytes take half the
+// L1 -> L2 requests.  Two stages (the remainder tile): K-step kt reads stage
+// kt % 2.  The one barrier per K-step sits in sub-step 3, after its first
+// row of MFMAs: every wavefront has then read its last fragments of stage kt
+// and has its share of stage kt+1 in LDS, so stage kt+1 is complete and
+// stage kt's slot is free.  Right after it the wavefront reads the fragments
+// of (kt+1, 0) and starts the loads of stage kt+2 into the freed slot, which
+// go on through sub-steps 0 and 1 of K-step kt+1; they have landed by the
+// barrier of K-step kt+1.
+//
+// Split rings (the full tile): the same sub-steps and barrier, but the
+// weights, which come from HBM, are loaded two K-steps ahead of their use
+// and the receive rows, mostly L2 hits, one.  One stage of 64 KiB in flight
+// per CU leaves the HBM stream short of bytes in flight; a third 64 KiB
+// stage does not fit, a third B slot of 32 KiB does.
 //
 // n_tile counts BN-wide column tiles (for gate/up: BN/2 intermediate
 // columns, gate and up interleaved in 32-row blocks); rows [row0, row0 +
@@ -220,8 +234,8 @@ static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTi
 // workgroup calls this with the same arguments.
 template <int BM, int BN, int STAGES, bool SWIGLU, int BK = kBK>
 __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
-                                         int n_tile, int row0, int rows_valid, int lag, int kb,
-                                         int nkt, float *part) {
+                                         int n_tile, int row0, int rows_valid, int kb, int nkt,
+                                         float *part) {
   constexpr int NW = kGemmWaves;
   constexpr int WM = BM / 128;          // wavefront rows
   constexpr int WN = NW / WM;           // wavefront columns
@@ -238,13 +252,20 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   constexpr int LB = BN / (RPI * NW);   // B loads per wavefront per stage
   constexpr int LPS = LA + LB;
   constexpr int KSUB = BK / 16;         // MFMA sub-steps per K-step
+  // K-steps of 64 with STAGES == 5: separate rings for the operands, two
+  // slots of A and three of B (each slot one K-step of one operand)
+  constexpr bool SPLIT = KSUB == 4 && STAGES == 5;
+  constexpr int B_BYTES = BN * ROWB;
+  constexpr int RING_A = SPLIT ? 2 : STAGES;         // A slots (or whole stages)
+  constexpr int B_RING_OFF = SPLIT ? RING_A * A_BYTES : A_BYTES;
+  constexpr int RING_BYTES = SPLIT ? 2 * A_BYTES + 3 * B_BYTES : STAGES * STAGE_BYTES;
   static_assert(WM * WN == NW && FM == 4 && FN == 4, "4 x 4 blocks of 32 x 32 per wavefront");
   static_assert((KSUB == 2 && STAGES >= 3 && (STAGES - 2) * LPS < 64) ||
-                    (KSUB == 4 && STAGES == 2 && LPS < 64),
-                "K-steps of 32 with 3 or more stages, or of 64 with two");
+                    (KSUB == 4 && (STAGES == 2 || STAGES == 5) && LPS < 64),
+                "K-steps of 32 with 3 or more stages, or of 64 with two stages or split rings");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
   static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
-  static_assert(STAGES * STAGE_BYTES <= kGemmLdsBytes, "the ring must fit the LDS");
+  static_assert(RING_BYTES <= kGemmLdsBytes, "the ring must fit the LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -257,7 +278,6 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   n_tile = uniform(n_tile);
   row0 = uniform(row0);
   rows_valid = uniform(rows_valid);
-  lag = uniform(lag);
   kb = uniform(kb);
   const int slot = e / a.eps;
   const int64_t grow0 = (int64_t)uniform(a.expert_off[e]) + row0;
@@ -301,25 +321,34 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   // one wavefront's blocks differ by multiples of 32, so they share the row
   // swizzle and differ by constant offsets (folded into the instructions).
   // Kept opaque so the compiler does not recompute them inside the loop.
-  uint32_t fa_addr[STAGES][KSUB], fb_addr[STAGES][KSUB];
+  // With split rings: A slot st for fa_addr, B slot 0 for fb_addr (slot s
+  // adds s * B_BYTES).
+  constexpr int NSA = RING_A, NSB = SPLIT ? 1 : STAGES;
+  uint32_t fa_addr[NSA][KSUB], fb_addr[NSB][KSUB];
   {
     const int l = lane & 31;
     const uint32_t base = lds_addr(smem);
+    constexpr int SLOT_A = SPLIT ? A_BYTES : STAGE_BYTES;
 #pragma unroll
-    for (int st = 0; st < STAGES; ++st)
+    for (int sk = 0; sk < KSUB; ++sk) {
+      const int c = sk * 2 + (lane >> 5);
+      const uint32_t lp = (uint32_t)(l * ROWB + ((c ^ swz<CPR>(l)) * 16));
 #pragma unroll
-      for (int sk = 0; sk < KSUB; ++sk) {
-        const int c = sk * 2 + (lane >> 5);
-        const uint32_t lp = (uint32_t)(l * ROWB + ((c ^ swz<CPR>(l)) * 16));
-        fa_addr[st][sk] = base + st * STAGE_BYTES + wm * 32 * ROWB + lp;
-        fb_addr[st][sk] = base + st * STAGE_BYTES + A_BYTES + wn * TN * ROWB + lp;
-        asm volatile("" : "+v"(fa_addr[st][sk]), "+v"(fb_addr[st][sk]));
+      for (int st = 0; st < NSA; ++st) {
+        fa_addr[st][sk] = base + st * SLOT_A + wm * 32 * ROWB + lp;
+        asm volatile("" : "+v"(fa_addr[st][sk]));
       }
+#pragma unroll
+      for (int st = 0; st < NSB; ++st) {
+        fb_addr[st][sk] = base + st * STAGE_BYTES + B_RING_OFF + wn * TN * ROWB + lp;
+        asm volatile("" : "+v"(fb_addr[st][sk]));
+      }
+    }
   }
 
   // load q (0 .. LPS-1: A loads, then B loads) of this wavefront's share of
-  // K-step kt (the tail re-loads the last one) into ring stage ST; K-steps
-  // run from kb + lag, wrapping inside [kb, kb + nk).  Scalar offsets only.
+  // K-step kt (K-steps kb, kb + 1, ...; past the range the tail re-loads
+  // the last one) into ring stage ST.  Scalar offsets only.
   auto issue_load = [&](auto st_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value, q = decltype(q_c)::value;
     char *sbase = smem + ST * STAGE_BYTES;
@@ -328,10 +357,18 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     else
       buffer_load_lds_16(rb, ob[q - LA], soff, sbase + A_BYTES + ((q - LA) * NW + wave) * 1024);
   };
+  // split rings: A load q into A slot SL; B load q into B slot bsl
+  // (wavefront-uniform)
+  auto issue_a = [&](auto sl_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
+    constexpr int SL = decltype(sl_c)::value, q = decltype(q_c)::value;
+    buffer_load_lds_16(ra, oa[q], soff, smem + SL * A_BYTES + (q * NW + wave) * 1024);
+  };
+  auto issue_b = [&](int bsl, auto q_c, uint32_t soff) __attribute__((always_inline)) {
+    constexpr int q = decltype(q_c)::value;
+    buffer_load_lds_16(rb, ob[q], soff, smem + B_RING_OFF + bsl * B_BYTES + (q * NW + wave) * 1024);
+  };
   auto k_offset = [&](int kt) __attribute__((always_inline)) {
-    int kc = (kt < nk ? kt : nk - 1) + lag;
-    if (kc >= nk) kc -= nk;
-    return (uint32_t)(kb + kc) * ROWB;
+    return (uint32_t)(kb + (kt < nk ? kt : nk - 1)) * ROWB;
   };
 
   // this wavefront's blocks (wm + WM i) holding rows: a prefix i < nact
@@ -372,11 +409,21 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
 
     // prologue: K-steps 0 .. STAGES-2 in flight; stage 0 complete
     // everywhere; the fragments of (K-step 0, sub-step 0) read into buffer 0
-    static_for<STAGES - 1>([&](auto p_c) __attribute__((always_inline)) {
-      const uint32_t soff = k_offset(decltype(p_c)::value);
-      static_for<LPS>([&](auto q_c) __attribute__((always_inline)) { issue_load(p_c, q_c, soff); });
-    });
-    wait_vmcnt<(STAGES - 2) * LPS>();
+    if constexpr (!SPLIT) {
+      static_for<STAGES - 1>([&](auto p_c) __attribute__((always_inline)) {
+        const uint32_t soff = k_offset(decltype(p_c)::value);
+        static_for<LPS>([&](auto q_c) __attribute__((always_inline)) { issue_load(p_c, q_c, soff); });
+      });
+      wait_vmcnt<(STAGES - 2) * LPS>();
+    } else {
+      // split rings: A and B of K-step 0, then B of K-step 1 (may stay in
+      // flight)
+      const uint32_t s0 = k_offset(0), s1 = k_offset(1);
+      static_for<LA>([&](auto q_c) __attribute__((always_inline)) { issue_a(I0{}, q_c, s0); });
+      static_for<LB>([&](auto q_c) __attribute__((always_inline)) { issue_b(0, q_c, s0); });
+      static_for<LB>([&](auto q_c) __attribute__((always_inline)) { issue_b(1, q_c, s1); });
+      wait_vmcnt<LB>();
+    }
     stage_barrier();
     static_for<NRD>([&](auto r_c) __attribute__((always_inline)) { read_frag(I0{}, I0{}, I0{}, r_c); });
 
@@ -461,7 +508,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     static_for<STAGES - 1>([&](auto p) __attribute__((always_inline)) {
       if (kt + decltype(p)::value < nk) step(p, kt + decltype(p)::value);
     });
-    } else {
+    } else if constexpr (!SPLIT) {
     // K-steps of 64: sub-steps 0..3 of K-step kt multiply fragment buffers
     // 0, 1, 0, 1 and, one item after each MFMA, read the next sub-step's
     // fragments into the other buffer and issue loads: [L3, L3 + L0) of
@@ -546,6 +593,125 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       step(I1{}, kt + 1);
     }
     if (kt < nk) step(I0{}, kt);
+    } else {
+    // Split rings (K-steps of 64): K-step kt reads A slot kt % 2 and B slot
+    // kt % 3.  After the barrier of K-step j the wavefront issues, in this
+    // order, its A loads of K-step j+2 and its B loads of K-step j+3 (the
+    // batch of j), spread as in the two-stage schedule: [0, L3) in sub-step 3
+    // of j, the rest in sub-steps 0 and 1 of j+1.  So at the barrier of
+    // K-step kt the last LB loads issued are the B loads of kt+2: after
+    // vmcnt(LB) the A and B loads of kt+1 have landed, and B streams two
+    // K-steps ahead of its use, A one.  The barrier frees A slot kt % 2 and B
+    // slot kt % 3, the targets of the next batch.
+    constexpr int L3 = LPS / 4, L0 = LPS / 2, L1 = LPS - L3 - L0;
+    // item q of a batch: A load q into A slot AS at K offset sa, or B load
+    // q - LA into B slot bsl at K offset sb
+    auto batch_item = [&](auto as_c, auto q_c, int bsl, uint32_t sa, uint32_t sb)
+                          __attribute__((always_inline)) {
+      constexpr int q = decltype(q_c)::value;
+      if constexpr (q < LA)
+        issue_a(as_c, q_c, sa);
+      else
+        issue_b(bsl, std::integral_constant<int, q - LA>{}, sb);
+    };
+    // fragment read r of a sub-step: B from the given address (the B slot is
+    // a runtime value), A from slot AST
+    auto read_frag_s = [&](auto buf_c, auto ast_c, auto sk_c, auto r_c, uint32_t fbsk)
+                           __attribute__((always_inline)) {
+      constexpr int BUF = decltype(buf_c)::value, AST = decltype(ast_c)::value;
+      constexpr int SK = decltype(sk_c)::value, r = decltype(r_c)::value;
+      if constexpr (r < FN)
+        fb[BUF][r] = *((lds_bf16x8_t *)(uintptr_t)fbsk + r * 32 * ROWB / 16);
+      else
+        fa[BUF][r - FN] =
+            *((lds_bf16x8_t *)(uintptr_t)fa_addr[AST][SK] + (r - FN) * WM * 32 * ROWB / 16);
+    };
+    auto substep = [&](auto bufm_c, auto rbuf_c, auto rast_c, auto rsk_c, uint32_t rfb,
+                       auto las_c, auto q0_c, auto nq_c, int lbs, uint32_t sa, uint32_t sb,
+                       auto sync_c) __attribute__((always_inline)) {
+      constexpr int BUFM = decltype(bufm_c)::value;  // buffer the MFMAs read
+      constexpr int RBUF = decltype(rbuf_c)::value;  // reads: into buffer RBUF,
+      constexpr int Q0 = decltype(q0_c)::value;      // batch items Q0 ..
+      constexpr int NQ = decltype(nq_c)::value;      //   .. Q0 + NQ - 1
+      constexpr bool SYNC = decltype(sync_c)::value;
+      constexpr int NIT = NRD + NQ;
+      auto item = [&](auto m_c) __attribute__((always_inline)) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m < NRD)
+          read_frag_s(std::integral_constant<int, RBUF>{}, rast_c, rsk_c,
+                      std::integral_constant<int, m>{}, rfb);
+        else
+          batch_item(las_c, std::integral_constant<int, Q0 + m - NRD>{}, lbs, sa, sb);
+      };
+      // the barrier of the K-step: this wavefront's reads of the current
+      // slots are done and its loads up to those of kt+1 have landed, then
+      // every wavefront's
+      auto sync = [&]() __attribute__((always_inline)) {
+        wait_lgkmcnt<0>();
+        wait_vmcnt<LB>();
+        stage_barrier();
+      };
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
+        constexpr int ISSUED = BEFORE < NRD ? BEFORE : NRD;
+        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUFM][i], fb[BUFM][j], acc[i][j],
+                                                              0, 0, 0);
+          if constexpr (!(SYNC && i == 0)) {
+            constexpr int m = BEFORE + j;
+            if constexpr (m < NIT) item(std::integral_constant<int, m>{});
+          }
+        });
+        if constexpr (SYNC && i == 0) sync();
+      });
+      if constexpr (SYNC && NACT == 0) sync();
+      constexpr int COVERED = NACT == 0 ? 0 : (SYNC ? (NACT - 1) * FN : NACT * FN);
+      static_for<(NIT > COVERED) ? NIT - COVERED : 0>([&](auto t_c) __attribute__((always_inline)) {
+        item(std::integral_constant<int, COVERED + decltype(t_c)::value>{});
+      });
+    };
+    using IT = std::true_type;
+    using IF = std::false_type;
+    auto step = [&](auto st_c, int kt, int bs) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;  // A slot of K-step kt
+      using S = std::integral_constant<int, ST>;
+      using N = std::integral_constant<int, 1 - ST>;
+      const int bs1 = bs == 2 ? 0 : bs + 1;     // B slot of kt+1
+      const int bs2 = bs1 == 2 ? 0 : bs1 + 1;   // B slot of kt+2 (and of kt-1)
+      const uint32_t s1 = k_offset(kt + 1), s2 = k_offset(kt + 2), s3 = k_offset(kt + 3);
+      const uint32_t bo = (uint32_t)bs * B_BYTES, bo1 = (uint32_t)bs1 * B_BYTES;
+      // the batch of kt-1 (A of kt+1, B of kt+2) in sub-steps 0 and 1
+      substep(I0{}, I1{}, S{}, I1{}, fb_addr[0][1] + bo, N{}, std::integral_constant<int, L3>{},
+              std::integral_constant<int, L0>{}, bs2, s1, s2, IF{});
+      substep(I1{}, I0{}, S{}, std::integral_constant<int, 2>{}, fb_addr[0][2] + bo, N{},
+              std::integral_constant<int, L3 + L0>{}, std::integral_constant<int, L1>{}, bs2, s1, s2,
+              IF{});
+      substep(I0{}, I1{}, S{}, std::integral_constant<int, 3>{}, fb_addr[0][3] + bo, N{}, I0{},
+              I0{}, bs2, s1, s2, IF{});
+      // barrier; fragments of (kt+1, 0); the first of the batch of kt (A of
+      // kt+2 into A slot ST, B of kt+3 into B slot bs)
+      substep(I1{}, I0{}, N{}, I0{}, fb_addr[0][0] + bo1, S{}, I0{},
+              std::integral_constant<int, L3>{}, bs, s2, s3, IT{});
+    };
+    // the first items of the batch of K-step -1: A of 1 (slot 1), B of 2
+    // (slot 2)
+    {
+      const uint32_t s1 = k_offset(1), s2 = k_offset(2);
+      static_for<L3>([&](auto q_c) __attribute__((always_inline)) {
+        batch_item(I1{}, q_c, 2, s1, s2);
+      });
+    }
+    int kt = 0, bs = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      step(I0{}, kt, bs);
+      bs = bs == 2 ? 0 : bs + 1;
+      step(I1{}, kt + 1, bs);
+      bs = bs == 2 ? 0 : bs + 1;
+    }
+    if (kt < nk) step(I0{}, kt, bs);
     }
     wait_lgkmcnt<0>();
     wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
