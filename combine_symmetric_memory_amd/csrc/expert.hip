@@ -16,7 +16,8 @@
 // walks the list: the tiles are split into kNumXcd contiguous ranges, one
 // per XCD, so the workgroups sharing an L2 work on neighbouring tiles -- the
 // m-tiles of one (expert, n-tile) reuse one weight panel, the n-tiles of one
-// expert reuse its receive rows.
+// expert reuse its receive rows.  Once its own range is done, a workgroup
+// takes what is left of the other XCDs' ranges.
 //
 // Inside a tile, 4 wavefronts (one per SIMD) interleave their MFMAs with
 // LDS fragment reads and with direct global -> LDS loads of a later K-step
@@ -101,11 +102,20 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   // (block id % kNumXcd, the hardware's round-robin placement) take the
   // tiles of range x in order from a counter, so the tiles running at once
   // on one XCD are neighbours and share weight panels and receive rows in
-  // that XCD's L2
+  // that XCD's L2.  Ranges split by tile count cost unevenly (remainder
+  // tiles run longer), so a workgroup whose range is exhausted takes tiles
+  // from the others' counters.
   const int xcd = blockIdx.x % kNumXcd;
-  const int t_begin = (int)((int64_t)total * xcd / kNumXcd);
-  const int t_end = (int)((int64_t)total * (xcd + 1) / kNumXcd);
   const int nk = g.kdim / kBK;
+  const int W = gridDim.x / kNumXcd;
+  // own range first; then, once it is exhausted, the other XCDs' ranges in
+  // turn (the tiles still left there at the end): the XCDs finish together
+  // whatever their ranges cost.  A unit is the same work on any XCD, so
+  // the result does not depend on who takes it.
+  for (int d = 0; d < kNumXcd; ++d) {
+  const int rx = (xcd + d) % kNumXcd;  // the range's XCD
+  const int t_begin = (int)((int64_t)total * rx / kNumXcd);
+  const int t_end = (int)((int64_t)total * (rx + 1) / kNumXcd);
 
   // The last round of an XCD's range is short when its U tiles leave a
   // small remainder R over the XCD's W workgroups.  Then the last R tiles
@@ -114,7 +124,6 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   // ranges in order once all of them are done.  The counter hands out
   // units: the U - R whole tiles (main launch), or the R * P ranges, tile
   // by tile (tail launch).
-  const int W = gridDim.x / kNumXcd;
   const int U = t_end - t_begin;
   const int R = U % W;
   int P = (g.allow_split && U < kSplitMaxRounds * W && R > 0 && 2 * R <= W)
@@ -125,7 +134,8 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   const int n_units = TAIL ? (P > 1 ? R * P : 0) : n_whole;
 
   for (;;) {
-    if (tid == 0) scratch[0] = atomicAdd(&g.queue[xcd], 1);
+    __syncthreads();  // every thread has read the previous unit
+    if (tid == 0) scratch[0] = atomicAdd(&g.queue[rx], 1);
     __syncthreads();
     // the unit and everything derived from it are wavefront-uniform: keep
     // them in scalar registers, so that per-K-step offsets stay scalar
@@ -156,16 +166,16 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
       const int piece = v % P;
       kb = piece * nk / P;
       nkt = (piece + 1) * nk / P - kb;
-      part = g.split_ws + (int64_t)(xcd * W + v) * kSplitTileFloats;
+      part = g.split_ws + (int64_t)(rx * W + v) * kSplitTileFloats;
       if (piece == 0 && tid == 0) {
-        int32_t *d = g.split_desc + (xcd * (W / 2) + v / P) * kSplitDescInts;
+        int32_t *d = g.split_desc + (rx * (W / 2) + v / P) * kSplitDescInts;
         d[0] = kind;
         d[1] = e;
         d[2] = n_tile;
         d[3] = row0;
         d[4] = rows_valid;
         d[5] = P;
-        d[6] = xcd * W + v;  // workspace slot of the first range
+        d[6] = rx * W + v;  // workspace slot of the first range
       }
     }
     if (kind == 2)
@@ -173,6 +183,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
                                                       kb, nkt, part);
     else
       run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid, kb, nkt, part);
+  }
   }
   // the last workgroup out has seen every counter exhausted: rearm them for
   // the next launch (ordered by the stream)
