@@ -352,6 +352,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's batch size T (routing drawn for T tokens)")
+    ap.add_argument("--inter", type=int, default=None,
+                    help="override the workload's SwiGLU width I (0: identity experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run one plain elementwise copy of 1 GiB "
@@ -372,7 +376,12 @@ def main():
     def log(*a):
         print("[bench]", *a, file=sys.stderr, flush=True)
 
-    cfg = get_config(args.workload)
+    over = {}
+    if args.tokens is not None:
+        over["T"] = args.tokens
+    if args.inter is not None:
+        over["I"] = args.inter
+    cfg = get_config(args.workload, **over)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log("workload", cfg)
@@ -521,7 +530,8 @@ def main():
         roofline["ridge_flop_per_byte"] = round(RIDGE_FLOP_PER_BYTE, 1)
     else:
         roofline = dict(kernel=dom, bound="hbm", **hbm)
-    roofline["traffic"] = profiled_traffic(cfg.name, dom)
+    # the profiled counters belong to the workload as configured
+    roofline["traffic"] = None if over else profiled_traffic(cfg.name, dom)
 
     # ---- calibrations: context for the stage rates, outside the step ----
     per_expert = None
