@@ -23,7 +23,10 @@
  *     - the expert is a SwiGLU MLP, h = silu(x Wg^T) * (x Wu^T) stored as
  *       bf16, y = h Wd^T stored as bf16;
  *     - combine is out[t] = bf16( sum_j w[t][j] * y_j ) accumulated in fp32
- *       with one fused multiply-add per j in j = 0..K-1 order.
+ *       with one fused multiply-add per j in j = 0..K-1 order;
+ *     - after an 8-bit dispatch the expert reads each value as
+ *       bf16( binary32( e4m3(q) * scale ) ), the scale of the value's block
+ *       of H / ns (orc_dequant_e4m3_rows).
  *
  * Precision: the GEMM-like sums are accumulated in double; h and y are
  * rounded to bf16 (round to nearest even) because the path stores them in
@@ -32,7 +35,8 @@
  *
  * Parity pins (tests/test_oracle_pins.py) check every function here against
  * brute force, library routines (numpy stable argsort, bincount, float64
- * matmul, torch bf16 conversion) and closed forms.
+ * matmul, torch bf16 and float8_e4m3fn conversions), exact rationals and
+ * closed forms.
  */
 #include <math.h>
 #include <pthread.h>
@@ -176,6 +180,51 @@ void orc_dispatch(const uint16_t *x, const float *w, const int32_t *idx,
       meta_src[row] = (int32_t)f;
       meta_w[row] = w[f];
       meta_e[row] = e;
+    }
+  }
+}
+
+/*
+ * OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent 0 holds the subnormals m * 2^-9; exponent 15 with
+ * mantissa 7 is NaN, and there are no infinities.  The value is exact in
+ * binary32.
+ */
+static float e4m3_to_f32(uint8_t b) {
+  int sign = b >> 7, ex = (b >> 3) & 15, m = b & 7;
+  float v;
+  if (ex == 15 && m == 7) return NAN;
+  if (ex == 0)
+    v = ldexpf((float)m, -9);
+  else
+    v = ldexpf((float)(8 + m), ex - 10);
+  return sign ? -v : v;
+}
+
+/*
+ * The expert's input when the dispatch moved 8-bit tokens (the pages hand
+ * the received scales on with the received tokens and leave their use to
+ * the expert): each receive row holds H e4m3 values and then ns fp32
+ * scales, scale i covering the values [i*H/ns, (i+1)*H/ns).  A value is
+ * decoded, multiplied by its scale in binary32 (one rounding to nearest
+ * even), and rounded to bf16 (nearest even) -- the bf16 the matrix cores
+ * then read.  ns == 0: no scales, the decoded value itself (exact in bf16).
+ * rows: n rows of 2H bytes; out: n rows of H bf16.
+ */
+void orc_dequant_e4m3_rows(const uint8_t *rows, int64_t n, int64_t H, int32_t ns,
+                           uint16_t *out) {
+  int64_t r, k;
+  int64_t blk = ns > 0 ? H / ns : H;
+  for (r = 0; r < n; ++r) {
+    const uint8_t *q = rows + r * 2 * H;
+    for (k = 0; k < H; ++k) {
+      float v = e4m3_to_f32(q[k]);
+      if (ns > 0) {
+        float sc;
+        memcpy(&sc, q + H + 4 * (k / blk), 4);
+        v = v * sc;
+      }
+      out[r * H + k] = orc_f32_to_bf16(v);
     }
   }
 }

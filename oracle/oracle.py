@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.orc_combine_rows.restype = None
         L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
         L.orc_f32_to_bf16.restype = ctypes.c_uint16
+        L.orc_dequant_e4m3_rows.argtypes = [P, i64, i64, i32, P]
+        L.orc_dequant_e4m3_rows.restype = None
         L.orc_f64_to_bf16.argtypes = [ctypes.c_double]
         L.orc_f64_to_bf16.restype = ctypes.c_uint16
         _lib = L
@@ -162,6 +164,20 @@ def dispatch_fp8(x8: np.ndarray, scales: np.ndarray, w: np.ndarray, idx: np.ndar
     lib().orc_dispatch_fp8(_p(x8), _p(scales), ns, _p(w), _p(idx), _p(pos), T, K, H, E, S, cap,
                            _p(rows), _p(ms), _p(mw), _p(me))
     return Dispatched(rows, ms, mw, me)
+
+
+def dequant_e4m3_rows(rows: np.ndarray, ns: int) -> np.ndarray:
+    """The bf16 expert input of 8-bit receive rows: rows [..., 2H] bytes
+    (H e4m3 values, then ns fp32 scales) -> bf16 bits [..., H]; each value
+    decoded, times its block's scale in binary32, rounded to bf16."""
+    rows = _c(rows, np.uint8)
+    shape = rows.shape
+    H = shape[-1] // 2
+    assert shape[-1] == 2 * H and ns >= 0 and 4 * ns <= H and (ns == 0 or H % ns == 0)
+    n = int(np.prod(shape[:-1]))
+    out = np.zeros(shape[:-1] + (H,), np.uint16)
+    lib().orc_dequant_e4m3_rows(_p(rows), n, H, ns, _p(out))
+    return out
 
 
 def swiglu_rows(X: np.ndarray, w13_e: np.ndarray, w2_e: np.ndarray,

@@ -493,3 +493,141 @@ def test_tiny_pipeline_brute_force(orc):
     o, rb = _f32(r.out), _f32(refb)
     assert np.abs(o - rb).max() <= 2e-2 * np.abs(rb).max()
     assert _ulp_diff(r.out, refb).max() <= 2
+
+
+# ---- the expert's input from 8-bit receive rows (oracle.dequant_e4m3_rows)
+
+def _e4m3_codes_f32():
+    """Every e4m3 code decoded by torch's float8_e4m3fn (a library routine)."""
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+
+
+def _rows_8bit(q: np.ndarray, scales: np.ndarray | None) -> np.ndarray:
+    """Receive rows [n, 2H]: the H code bytes, then the fp32 scales' bytes."""
+    n, H = q.shape
+    rows = np.zeros((n, 2 * H), np.uint8)
+    rows[:, :H] = q
+    if scales is not None:
+        rows[:, H:H + 4 * scales.shape[1]] = np.ascontiguousarray(scales, np.float32).view(np.uint8)
+    return rows
+
+
+def test_e4m3_decode_on_every_code():
+    """With no scales the expert input is the decoded value itself: every
+    finite code against torch's e4m3fn decode (exact in bf16), the two NaN
+    codes to a NaN."""
+    from oracle import oracle as orc
+    q = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    got = orc.dequant_e4m3_rows(_rows_8bit(q, None), 0)[0]
+    ref = _e4m3_codes_f32()
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            assert (got[c] & 0x7F80) == 0x7F80 and (got[c] & 0x7F) != 0, c
+            continue
+        bits = int(np.array([ref[c]], np.float32).view(np.uint32)[0])
+        assert bits & 0xFFFF == 0, c  # e4m3 values are bf16 values
+        assert got[c] == bits >> 16, (c, got[c], bits >> 16)
+
+
+def _exact_two_step(code_val: float, s: float) -> int:
+    """bf16 of round_binary32(code * s), from exact rationals (a zero
+    product keeps the IEEE sign of the factors)."""
+    p = Fraction(float(code_val)) * Fraction(float(s))
+    if p == 0:
+        return 0x8000 if np.copysign(1.0, code_val) * np.copysign(1.0, s) < 0 else 0
+    return _bf16_of(_round_rational(_round_rational(p, 24), 8))
+
+
+def _exact_one_step(code_val: float, s: float) -> int:
+    p = Fraction(float(code_val)) * Fraction(float(s))
+    return _bf16_of(_round_rational(p, 8))
+
+
+def _is_tie(p: Fraction, prec: int) -> bool:
+    """p lies exactly half-way between two numbers of `prec` significant bits."""
+    if p == 0:
+        return False
+    a = abs(p)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    n = a / Fraction(2) ** (max(e, -126) - (prec - 1))
+    return n - n.numerator // n.denominator == Fraction(1, 2)
+
+
+def _dequant_witnesses(seed: int = 7):
+    """(code, scale) pairs: exact products that are binary32 ties; binary32
+    products that are bf16 ties; and products that the binary32 rounding
+    moves onto a bf16 tie, so that rounding twice gives another bf16 than
+    rounding the exact product once."""
+    rng = np.random.default_rng(seed)
+    vals = _e4m3_codes_f32()
+    code_of = {float(vals[c]): c for c in range(128) if np.isfinite(vals[c])}
+    # binary32 ties: a 4-bit significand times a random 24-bit one
+    f32_ties = []
+    multi = [code_of[v] for v in (1.125, 1.375, 1.625, 1.875, 1.25, 1.75)]
+    while len(f32_ties) < 8:
+        c = int(rng.choice(multi))
+        s = float(np.float32(rng.uniform(1.0, 2.0) * 2.0 ** int(rng.integers(-20, 20))))
+        if _is_tie(Fraction(float(vals[c])) * Fraction(s), 24):
+            f32_ties.append((c, s))
+    # bf16 ties: 1.0 times a binary32 whose low 16 bits are 0x8000
+    one = code_of[1.0]
+    bf16_ties = []
+    for k in range(8):
+        upper = (0x3F00 + (k << 7) + 2 * int(rng.integers(0, 64))) & 0x7FFF
+        bf16_ties.append((one, float(np.array([(upper << 16) | 0x8000], np.uint32).view(np.float32)[0])))
+    # double rounding: binary32 F a bf16 tie with an even upper half; a scale
+    # near F / q whose exact product rounds to F in binary32 but lies above it
+    double = []
+    for k in range(64):
+        if len(double) >= 8:
+            break
+        upper = 0x3F00 + 2 * int(rng.integers(0, 1 << 10))
+        F = float(np.array([(upper << 16) | 0x8000], np.uint32).view(np.float32)[0])
+        c = multi[k % len(multi)]
+        qv = float(vals[c])
+        s0 = np.float32(F / qv)
+        for step in range(-40, 41):
+            s = float(np.nextafter(s0, np.float32(np.inf if step > 0 else -np.inf)) if step else s0)
+            for _ in range(abs(step) - 1):
+                s = float(np.nextafter(np.float32(s), np.float32(np.inf if step > 0 else -np.inf)))
+            p = Fraction(qv) * Fraction(s)
+            if p > Fraction(F) and _round_rational(p, 24) == Fraction(F):
+                double.append((c, s))
+                break
+    return f32_ties, bf16_ties, double
+
+
+def test_dequant_rounds_the_scaled_value_twice_to_nearest_even():
+    """Decoded value times its block's scale, rounded to binary32 and then to
+    bf16 (both to nearest even): against exact rationals on random codes and
+    scales, on exact binary32 ties, on exact bf16 ties, and on cases where
+    one rounding of the exact product would give another bf16."""
+    from oracle import oracle as orc
+    vals = _e4m3_codes_f32()
+    f32_ties, bf16_ties, double = _dequant_witnesses()
+    assert len(double) >= 4 and len(bf16_ties) == 8
+    rng = np.random.default_rng(3)
+    finite = np.array([c for c in range(256) if np.isfinite(vals[c])], np.uint8)
+    for ns in (1, 2, 4):
+        H = 256
+        q = rng.choice(finite, size=(3, H)).astype(np.uint8)
+        sc = (rng.uniform(0.5, 2.0, (3, ns)) * 2.0 ** rng.integers(-12, 12, (3, ns))).astype(np.float32)
+        # plant the witnesses at the start of row 0 (their scale is block 0's)
+        wit = f32_ties + bf16_ties + double
+        for i, (c, s) in enumerate(wit[:min(len(wit), H // ns)]):
+            q[0, i] = c
+        got = orc.dequant_e4m3_rows(_rows_8bit(q, sc), ns)
+        blk = H // ns
+        for r in range(3):
+            for k in range(H):
+                want = _exact_two_step(vals[q[r, k]], sc[r, k // blk])
+                assert got[r, k] == want, (ns, r, k, got[r, k], want)
+    # the witnesses themselves, one scale each (ns = number of them, blocks of 1)
+    for c, s in f32_ties + bf16_ties + double:
+        q = np.full((1, 64), c, np.uint8)
+        sc = np.full((1, 1), s, np.float32)
+        got = orc.dequant_e4m3_rows(_rows_8bit(q, sc), 1)[0, 0]
+        assert got == _exact_two_step(vals[c], s), (c, s)
+    assert any(_exact_two_step(vals[c], s) != _exact_one_step(vals[c], s) for c, s in double)
