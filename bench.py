@@ -75,6 +75,59 @@ def stage_work(cfg, active_experts=None):
     return w
 
 
+def fp8_step_variant(cfg, moe, idx, x8, sc, w, w13, w2, out, stream, flush, n_iter, steps,
+                     ms_per_step, stages, work, torch):
+    """The whole step on 8-bit tokens: plan, the 8-bit dispatch, the expert
+    reading the 8-bit receive rows and their scales in place, combine.
+    Timed like the bf16 step (wall clock over `steps` steps), then per
+    kernel with HIP events, caches flushed before each step."""
+    import numpy as np
+
+    def step8():
+        moe.plan(idx, stream)
+        moe.dispatch_fp8(x8, sc, w, stream)
+        moe.expert(w13, w2, stream)
+        moe.combine(w, out=out, stream=stream)
+
+    for _ in range(3):
+        step8()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step8()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    per = {}
+    moe.set_timing(True)
+    for _ in range(n_iter):
+        flush()
+        step8()
+        torch.cuda.synchronize()
+        for k, (n, t) in moe.timing_summary().items():
+            if n:
+                per.setdefault(k, []).append(t / n)
+    moe.set_timing(False)
+    ns = sc.shape[1]
+    TK = cfg.T * cfg.K
+    gu = dict(work["expert_gate_up"])
+    # the 8-bit rows: H codes and ns scales per row instead of 2H bytes
+    gu["bytes"] += TK * (cfg.H + 4 * ns) - 2 * TK * cfg.H
+    res = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+           "vs_bf16_step_time": round(ms / ms_per_step, 4), "stages": {}}
+    for k, times in per.items():
+        avg = float(np.mean(times))
+        st = {"avg_ms": round(avg, 5), "median_ms": round(float(np.median(times)), 5)}
+        if k in stages:
+            st["vs_bf16"] = round(avg / stages[k]["avg_ms"], 3)
+        if k == "expert_gate_up":
+            st["alg_bytes"] = gu["bytes"]
+            st["GB_s"] = round(gu["bytes"] / (avg * 1e-3) / 1e9, 1)
+            st["TFLOP_s"] = round(gu["flops"] / (avg * 1e-3) / 1e12, 2)
+            st["mfma_frac"] = round(st["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)
+        res["stages"][k] = st
+    return res
+
+
 def code_digest(path):
     """sha256 of a C++/HIP source with its // comments, trailing blanks and
     empty lines removed: a change to the comments keeps the digest."""
@@ -491,10 +544,6 @@ def main():
             n, ms = moe.timing_summary()["dispatch_fp8"]
             times.append(ms / n)
         moe.set_timing(False)
-        # the bf16 rows back in the receive window for what follows
-        moe.dispatch(x, w, stream)
-        torch.cuda.synchronize()
-        del x8, sc
         t = np.asarray(times)
         TK = cfg.T * cfg.K
         nbytes = cfg.T * cfg.H + TK * cfg.H + 4 * ns * (cfg.T + TK) + 24 * TK
@@ -505,6 +554,14 @@ def main():
             "GB_s": round(nbytes / (avg * 1e-3) / 1e9, 1),
             "hbm_frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "vs_bf16_dispatch_time": round(avg / stages["dispatch"]["avg_ms"], 3)}
+        if cfg.I > 0:
+            variants["step_fp8"] = fp8_step_variant(cfg, moe, idx, x8, sc, w, w13, w2, out,
+                                                    stream, flush, n_iter, args.steps,
+                                                    ms_per_step, stages, work, torch)
+        # the bf16 rows back in the receive window for what follows
+        moe.dispatch(x, w, stream)
+        torch.cuda.synchronize()
+        del x8, sc
         log("variants", json.dumps(variants))
 
     if cfg.I > 0:

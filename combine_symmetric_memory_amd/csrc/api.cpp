@@ -64,6 +64,7 @@ struct cco_moe {
   int32_t max_plan_blocks = 0;
   int32_t planned_T = -1;  // T of the last plan (host-side order check)
   bool disp_8bit = false;  // the last dispatch moved 8-bit tokens with scales
+  int32_t disp_ns = 0;     // ... and that many scales per token
   int num_cus = 0;
   cco::FusedBuffers fused{};
   bool timing = false;
@@ -443,6 +444,7 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
   m->disp_8bit = true;
+  m->disp_ns = ns;
   if (T == 0) return CCO_OK;
   MoeArgs a = m->args;
   return timed_launch(m, 7, st, [&] {
@@ -454,8 +456,18 @@ int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *st
   if (!m || m->planned_T < 0) return CCO_ERR_INVALID_ARG;
   if (m->shape.inter == 0) return CCO_OK;  // identity experts
   if (!w13 || !w2 || !aligned(w13, 16) || !aligned(w2, 16)) return CCO_ERR_INVALID_ARG;
-  // the bf16 SwiGLU cannot read 8-bit receive rows
-  if (m->disp_8bit) return CCO_ERR_INVALID_ARG;
+  // 8-bit receive rows: their scale blocks must be whole runs of K-steps
+  // of 64 (a power of two of them), or absent
+  int32_t a8_ns = -1;
+  if (m->disp_8bit) {
+    const int32_t ns = m->disp_ns, H = m->shape.hidden;
+    if (ns > 0) {
+      if (H % ns != 0) return CCO_ERR_INVALID_ARG;
+      const int32_t ksteps = (H / ns) / 64;
+      if ((H / ns) % 64 != 0 || (ksteps & (ksteps - 1)) != 0) return CCO_ERR_INVALID_ARG;
+    }
+    a8_ns = ns;
+  }
   DeviceGuard dg(m->heap->device);
   if (!dg.ok) return CCO_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
@@ -463,7 +475,7 @@ int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *st
   MoeArgs a = m->args;
   const int32_t T = m->planned_T;
   int rc = timed_launch(m, 3, st,
-                        [&] { return cco::launch_expert_gate_up(a, w13, T, m->num_cus, st); });
+                        [&] { return cco::launch_expert_gate_up(a, w13, T, m->num_cus, a8_ns, st); });
   if (rc != CCO_OK) return rc;
   return timed_launch(m, 4, st,
                       [&] { return cco::launch_expert_down(a, w2, T, m->num_cus, st); });

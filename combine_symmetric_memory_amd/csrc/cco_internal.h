@@ -139,9 +139,12 @@ hipError_t launch_fused(const MoeArgs &a, const FusedBuffers &b, const int32_t *
                         hipStream_t st);
 
 // Expert GEMMs of the T planned tokens.  `num_cus` sizes the persistent
-// grids.
+// grids.  a8_ns < 0: the receive rows are bf16; otherwise they are the
+// 8-bit rows of an 8-bit dispatch with a8_ns scales each (H / a8_ns a
+// power-of-two multiple of 64 when a8_ns > 0), read as
+// bf16(binary32(e4m3 * scale)) by gate/up.
 hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int32_t T, int num_cus,
-                                 hipStream_t st);
+                                 int32_t a8_ns, hipStream_t st);
 hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int32_t T, int num_cus,
                               hipStream_t st);
 

@@ -38,7 +38,9 @@ namespace {
 // TAIL = false runs the whole tiles; TAIL = true, launched after it, the
 // K-ranges of the split tiles (each instantiation keeps only its own
 // epilogue, so the main one's register allocation is not disturbed).
-template <bool SWIGLU, bool TAIL>
+// A8: the A rows are the 8-bit receive rows of an 8-bit dispatch (gate/up
+// only), read as bf16(binary32(e4m3 * scale)).
+template <bool SWIGLU, bool TAIL, bool A8 = false>
 __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArgs a, GemmDesc g) {
   constexpr int NT = kGemmWaves * kWave;
   // The ring of the running tile shape takes all of the LDS.  Between tiles
@@ -179,10 +181,11 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
       }
     }
     if (kind == 2)
-      run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid,
-                                                      kb, nkt, part);
+      run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU, kBK, A8>(a, g, smem, e, n_tile, row0,
+                                                               rows_valid, kb, nkt, part);
     else
-      run_tile<kBM, kBN, kStages, SWIGLU>(a, g, smem, e, n_tile, row0, rows_valid, kb, nkt, part);
+      run_tile<kBM, kBN, kStages, SWIGLU, kBK, A8>(a, g, smem, e, n_tile, row0, rows_valid, kb,
+                                                   nkt, part);
   }
   }
   // the last workgroup out has seen every counter exhausted: rearm them for
@@ -278,19 +281,19 @@ constexpr size_t kGemmLds =
 // when it can have fewer than kSplitMaxRounds rounds: every expert's rows R
 // take at least ntiles * R / kBM tiles, so T * K routed rows take at least
 // ntiles * T * K / kBM.
-template <bool SWIGLU>
+template <bool SWIGLU, bool A8 = false>
 hipError_t launch_gemm(const MoeArgs &a, GemmDesc g, int32_t T, int num_cus, hipStream_t st) {
   const int nwg = gemm_workgroups(num_cus);
   const int64_t min_tiles = (int64_t)g.ntiles * T * a.K / kBM;
   g.allow_split = min_tiles < (int64_t)kSplitMaxRounds * nwg;
-  hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, false>), dim3(nwg), dim3(kGemmWaves * kWave),
+  hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, false, A8>), dim3(nwg), dim3(kGemmWaves * kWave),
                      kGemmLds, st, a, g);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !g.allow_split) return err;
   // the split tiles' K-ranges, with counters of their own
   GemmDesc gt = g;
   gt.queue = g.queue + 2 * (kNumXcd + 1);
-  hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, true>), dim3(nwg), dim3(kGemmWaves * kWave),
+  hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, true, A8>), dim3(nwg), dim3(kGemmWaves * kWave),
                      kGemmLds, st, a, gt);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -304,12 +307,19 @@ hipError_t launch_gemm(const MoeArgs &a, GemmDesc g, int32_t T, int num_cus, hip
 }  // namespace
 
 hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int32_t T, int num_cus,
-                                 hipStream_t st) {
+                                 int32_t a8_ns, hipStream_t st) {
   GemmDesc g = gemm_desc_gate_up(a, w13);
   g.queue = a.gemm_queue;
   g.split_ws = a.split_ws;
   g.split_desc = a.split_desc;
-  return launch_gemm<true>(a, g, T, num_cus, st);
+  if (a8_ns < 0) return launch_gemm<true>(a, g, T, num_cus, st);
+  // 8-bit rows: blocks of H / ns values, 2^kshift K-steps each (checked by
+  // the caller: a power of two)
+  g.a8_ns = a8_ns;
+  g.a8_kshift = 0;
+  if (a8_ns > 0)
+    while ((kBK << g.a8_kshift) < a.H / a8_ns) ++g.a8_kshift;
+  return launch_gemm<true, true>(a, g, T, num_cus, st);
 }
 
 hipError_t launch_expert_down(const MoeArgs &a, const uint16_t *w2, int32_t T, int num_cus,

@@ -49,6 +49,11 @@ struct GemmDesc {
   int32_t allow_split;   // nonzero: the tail and fixup launches follow this GEMM
   float *split_ws;       // fp32 partial sums of split tiles: one slot per workgroup
   int32_t *split_desc;   // [workgroups / 2][kSplitDescInts] split tiles, kind 0 = free
+  // 8-bit A rows (gate/up after an 8-bit dispatch): each row holds kdim e4m3
+  // values and then a8_ns fp32 scales, one per block of kdim / a8_ns values
+  // = 2^a8_kshift K-steps of 64; a8_ns == 0: no scales
+  int32_t a8_ns;
+  int32_t a8_kshift;
 };
 
 // Rows of expert e that fit its slot (a slot overflow is reported by the
@@ -127,6 +132,38 @@ __device__ __forceinline__ void buffer_load_lds_16(__amdgpu_buffer_rsrc_t r, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 16, (int)voff, (int)soff,
                                            0, 0);
 }
+// The same with 4 bytes per lane (lane l's dword lands at lds_base + 4 l).
+__device__ __forceinline__ void buffer_load_lds_4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_base, 4, (int)voff, (int)soff,
+                                           0, 0);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2_t;
+typedef __attribute__((address_space(3))) const float lds_f32_t;
+
+// Eight OCP e4m3 values (bytes in K order) times their fp32 scale, as the
+// bf16 A fragment of one MFMA: each value decoded exactly
+// (v_cvt_pk_f32_fp8), multiplied by s in binary32 and rounded to bf16
+// (v_cvt_pk_bf16_f32), both roundings to nearest even.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 q, float s) {
+  const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false);
+  const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+  const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false);
+  const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+  bf16x8 r;
+  r[0] = (__bf16)(f0.x * s);
+  r[1] = (__bf16)(f0.y * s);
+  r[2] = (__bf16)(f1.x * s);
+  r[3] = (__bf16)(f1.y * s);
+  r[4] = (__bf16)(f2.x * s);
+  r[5] = (__bf16)(f2.y * s);
+  r[6] = (__bf16)(f3.x * s);
+  r[7] = (__bf16)(f3.y * s);
+  return r;
+}
 
 // LDS tile layout: rows of BK bf16 (ROWB bytes), unpadded, 16-byte chunks
 // XOR-swizzled per row so that the 16 rows one fragment read touches fall
@@ -167,8 +204,10 @@ constexpr int kGemmLdsBytes = 160 * 1024;
 
 // LDS bytes of a tile's ring (STAGES == 5 with K-steps of 64: two A slots
 // and three B slots)
-constexpr int ring_bytes(int bm, int bn, int stages, int bk) {
-  return (bk == 64 && stages == 5) ? (2 * bm + 3 * bn) * bk * 2 : stages * (bm + bn) * bk * 2;
+constexpr int ring_bytes(int bm, int bn, int stages, int bk, bool a8 = false) {
+  const int a = a8 ? bm * bk + 1024 : bm * bk * 2;  // A slot: rows (and 8-bit rows' scales)
+  const int b = bn * bk * 2;
+  return (bk == 64 && stages == 5) ? 2 * a + 3 * b : stages * (a + b);
 }
 
 // Wavefronts per workgroup: one per SIMD.
@@ -232,7 +271,7 @@ static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTi
 // otherwise the fp32 sums of this K-range are written to part, row-major
 // [BM][BN] in the accumulators' column order.  Every wavefront of the
 // workgroup calls this with the same arguments.
-template <int BM, int BN, int STAGES, bool SWIGLU, int BK = kBK>
+template <int BM, int BN, int STAGES, bool SWIGLU, int BK = kBK, bool A8 = false>
 __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
                                          int n_tile, int row0, int rows_valid, int kb, int nkt,
                                          float *part) {
@@ -243,12 +282,19 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   constexpr int FN = TN / 32;           // 32-column blocks per wavefront
   constexpr int MB = BM / 32;           // 32-row blocks per tile
   constexpr int FM = MB / WM;           // 32-row blocks per wavefront
-  constexpr int ROWB = BK * 2;          // bytes per LDS row
+  constexpr int ROWB = BK * 2;          // bytes per LDS row (B, and bf16 A)
   constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
   constexpr int RPI = 1024 / ROWB;      // rows filled by one 1 KiB wavefront load
-  constexpr int A_BYTES = BM * ROWB;
-  constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-  constexpr int LA = BM / (RPI * NW);   // A loads per wavefront per stage
+  // A8: 8-bit A rows, BK bytes per row, and after them the K-step's row
+  // scales (one wavefront load of 64 rows' dwords each, 256 rows' worth)
+  constexpr int ROWB_A = A8 ? BK : ROWB;
+  constexpr int CPR_A = ROWB_A / 16;
+  constexpr int RPI_A = 1024 / ROWB_A;
+  constexpr int A_DATA = BM * ROWB_A;
+  constexpr int A_BYTES = A_DATA + (A8 ? 1024 : 0);
+  constexpr int STAGE_BYTES = A_BYTES + BN * ROWB;
+  constexpr int LAD = BM / (RPI_A * NW);     // A row loads per wavefront per stage
+  constexpr int LA = LAD + (A8 ? 1 : 0);     // ... and the scale load
   constexpr int LB = BN / (RPI * NW);   // B loads per wavefront per stage
   constexpr int LPS = LA + LB;
   constexpr int KSUB = BK / 16;         // MFMA sub-steps per K-step
@@ -263,8 +309,9 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   static_assert((KSUB == 2 && STAGES >= 3 && (STAGES - 2) * LPS < 64) ||
                     (KSUB == 4 && (STAGES == 2 || STAGES == 5) && LPS < 64),
                 "K-steps of 32 with 3 or more stages, or of 64 with two stages or split rings");
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
-  static_assert(32 % RPI == 0, "a load must not straddle two 32-row blocks");
+  static_assert(BM % (RPI_A * NW) == 0 && BN % (RPI * NW) == 0, "tile / wavefront mismatch");
+  static_assert(32 % RPI == 0 && 32 % RPI_A == 0, "a load must not straddle two 32-row blocks");
+  static_assert(!A8 || (KSUB == 4 && BM <= 256), "8-bit A: K-steps of 64, at most 256 rows");
   static_assert(RING_BYTES <= kGemmLdsBytes, "the ring must fit the LDS");
 
   const int tid = threadIdx.x;
@@ -296,11 +343,21 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   const int ld_pchunk = lane % CPR;
   uint32_t oa[LA], ob[LB];
 #pragma unroll
-  for (int q = 0; q < LA; ++q) {
-    const int row = (q * NW + wave) * RPI + ld_row;
+  for (int q = 0; q < LAD; ++q) {
+    const int row = (q * NW + wave) * RPI_A + lane / CPR_A;
     const int rr = row < rows_valid ? row : rows_valid - 1;
-    oa[q] = (uint32_t)rr * (uint32_t)g.lda * 2u + (uint32_t)((ld_pchunk ^ swz<CPR>(row)) * 16);
+    oa[q] = (uint32_t)rr * (uint32_t)g.lda * 2u +
+            (uint32_t)(((lane % CPR_A) ^ swz<CPR_A>(row)) * 16);
     asm volatile("" : "+v"(oa[q]));
+  }
+  if constexpr (A8) {
+    // the scale load: row wave * 64 + lane (rows past the tile's re-read
+    // the last row; their scales are never used); scales follow the kdim
+    // value bytes of the row
+    const int row = wave * kWave + lane;
+    const int rr = row < rows_valid ? row : rows_valid - 1;
+    oa[LAD] = (uint32_t)rr * (uint32_t)g.lda * 2u + (uint32_t)g.kdim;
+    asm volatile("" : "+v"(oa[LAD]));
   }
 #pragma unroll
   for (int q = 0; q < LB; ++q) {
@@ -325,17 +382,30 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   // adds s * B_BYTES).
   constexpr int NSA = RING_A, NSB = SPLIT ? 1 : STAGES;
   uint32_t fa_addr[NSA][KSUB], fb_addr[NSB][KSUB];
+  // A8: the address of this lane's row scale (row block wm) in each A slot
+  uint32_t fsc_addr[A8 ? NSA : 1];
   {
     const int l = lane & 31;
     const uint32_t base = lds_addr(smem);
     constexpr int SLOT_A = SPLIT ? A_BYTES : STAGE_BYTES;
+    if constexpr (A8) {
+#pragma unroll
+      for (int st = 0; st < NSA; ++st) {
+        fsc_addr[st] = base + st * SLOT_A + A_DATA + (wm * 32 + l) * 4;
+        asm volatile("" : "+v"(fsc_addr[st]));
+      }
+    }
 #pragma unroll
     for (int sk = 0; sk < KSUB; ++sk) {
       const int c = sk * 2 + (lane >> 5);
       const uint32_t lp = (uint32_t)(l * ROWB + ((c ^ swz<CPR>(l)) * 16));
+      // 8-bit A: the sub-step's 16 values of row l are one 16-byte chunk;
+      // lanes 32..63 take its second half
+      const uint32_t lpa =
+          A8 ? (uint32_t)(l * ROWB_A + ((sk ^ swz<CPR_A>(l)) * 16) + (lane >> 5) * 8) : lp;
 #pragma unroll
       for (int st = 0; st < NSA; ++st) {
-        fa_addr[st][sk] = base + st * SLOT_A + wm * 32 * ROWB + lp;
+        fa_addr[st][sk] = base + st * SLOT_A + wm * 32 * ROWB_A + lpa;
         asm volatile("" : "+v"(fa_addr[st][sk]));
       }
 #pragma unroll
@@ -346,14 +416,25 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     }
   }
 
+  // the K-step's byte offset into an A row (soff is the B rows' offset, 2
+  // bytes per value), and the byte offset of its scale within the row's
+  // scales (soff / ROWB is the K-step)
+  auto a_koff = [&](uint32_t soff) __attribute__((always_inline)) {
+    return A8 ? soff >> 1 : soff;
+  };
+  auto a_scoff = [&](uint32_t soff) __attribute__((always_inline)) {
+    return ((soff / ROWB) >> g.a8_kshift) * 4u;
+  };
   // load q (0 .. LPS-1: A loads, then B loads) of this wavefront's share of
   // K-step kt (K-steps kb, kb + 1, ...; past the range the tail re-loads
   // the last one) into ring stage ST.  Scalar offsets only.
   auto issue_load = [&](auto st_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value, q = decltype(q_c)::value;
     char *sbase = smem + ST * STAGE_BYTES;
-    if constexpr (q < LA)
-      buffer_load_lds_16(ra, oa[q], soff, sbase + (q * NW + wave) * 1024);
+    if constexpr (q < LAD)
+      buffer_load_lds_16(ra, oa[q], a_koff(soff), sbase + (q * NW + wave) * 1024);
+    else if constexpr (q < LA)
+      buffer_load_lds_4(ra, oa[q], a_scoff(soff), sbase + A_DATA + wave * 256);
     else
       buffer_load_lds_16(rb, ob[q - LA], soff, sbase + A_BYTES + ((q - LA) * NW + wave) * 1024);
   };
@@ -361,7 +442,10 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
   // (wavefront-uniform)
   auto issue_a = [&](auto sl_c, auto q_c, uint32_t soff) __attribute__((always_inline)) {
     constexpr int SL = decltype(sl_c)::value, q = decltype(q_c)::value;
-    buffer_load_lds_16(ra, oa[q], soff, smem + SL * A_BYTES + (q * NW + wave) * 1024);
+    if constexpr (q < LAD)
+      buffer_load_lds_16(ra, oa[q], a_koff(soff), smem + SL * A_BYTES + (q * NW + wave) * 1024);
+    else
+      buffer_load_lds_4(ra, oa[q], a_scoff(soff), smem + SL * A_BYTES + A_DATA + wave * 256);
   };
   auto issue_b = [&](int bsl, auto q_c, uint32_t soff) __attribute__((always_inline)) {
     constexpr int q = decltype(q_c)::value;
@@ -394,15 +478,41 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     // fragments of the two sub-steps (double buffer: one is multiplied while
     // the other is read).  Read order: the FN B fragments, then the NACT A
     // fragments, so that row i of MFMAs can start once A fragment i is in.
-    bf16x8 fa[2][NF], fb[2][FN];
+    // A8: the A fragments are 8 bytes of e4m3 values; sc[s][i] is the scale
+    // of row block i in A slot s, read with the first fragments of its
+    // K-step (before them, so that waiting for a fragment covers it).
+    std::conditional_t<A8, u32x2, bf16x8> fa[2][NF];
+    bf16x8 fb[2][FN];
+    float sc[2][NF];
+    constexpr int NSC = A8 ? NACT : 0;  // scale reads with a K-step's first fragments
+    const bool unit_scale = !A8 || g.a8_ns == 0;
     auto read_frag = [&](auto buf_c, auto st_c, auto sk_c, auto r_c) __attribute__((always_inline)) {
       constexpr int BUF = decltype(buf_c)::value, ST = decltype(st_c)::value;
       constexpr int SK = decltype(sk_c)::value, r = decltype(r_c)::value;
       if constexpr (r < FN)
         fb[BUF][r] = *((lds_bf16x8_t *)(uintptr_t)fb_addr[ST][SK] + r * 32 * ROWB / 16);
+      else if constexpr (A8)
+        fa[BUF][r - FN] =
+            *(lds_u32x2_t *)(uintptr_t)(fa_addr[ST][SK] + (r - FN) * WM * 32 * ROWB_A);
       else
         fa[BUF][r - FN] =
             *((lds_bf16x8_t *)(uintptr_t)fa_addr[ST][SK] + (r - FN) * WM * 32 * ROWB / 16);
+    };
+    auto read_scale = [&](auto st_c, auto i_c) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value, i = decltype(i_c)::value;
+      if constexpr (A8) {
+        const float v = *(lds_f32_t *)(uintptr_t)(fsc_addr[ST] + i * WM * 32 * 4);
+        sc[ST][i] = unit_scale ? 1.0f : v;
+      }
+    };
+    // the bf16 A fragment of row i of the MFMAs: buffer BUFM, K-step of A slot MST
+    auto a_frag = [&](auto bufm_c, auto mst_c, auto i_c) __attribute__((always_inline)) {
+      constexpr int BUFM = decltype(bufm_c)::value, MST = decltype(mst_c)::value;
+      constexpr int i = decltype(i_c)::value;
+      if constexpr (A8)
+        return e4m3x8_to_bf16(fa[BUFM][i], sc[MST][i]);
+      else
+        return fa[BUFM][i];
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -425,6 +535,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       wait_vmcnt<LB>();
     }
     stage_barrier();
+    static_for<NSC>([&](auto i_c) __attribute__((always_inline)) { read_scale(I0{}, i_c); });
     static_for<NRD>([&](auto r_c) __attribute__((always_inline)) { read_frag(I0{}, I0{}, I0{}, r_c); });
 
     if constexpr (KSUB == 2) {
@@ -517,7 +628,8 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     // [0, L3) of stage kt+2 into the slot stage kt used.
     constexpr int L3 = LPS / 4, L0 = LPS / 2, L1 = LPS - L3 - L0;
     auto substep = [&](auto bufm_c, auto rbuf_c, auto rst_c, auto rsk_c, auto lst_c, auto q0_c,
-                       auto nq_c, uint32_t soff, auto sync_c) __attribute__((always_inline)) {
+                       auto nq_c, uint32_t soff, auto sync_c, auto mst_c)
+                       __attribute__((always_inline)) {
       constexpr int BUFM = decltype(bufm_c)::value;  // buffer the MFMAs read
       constexpr int RBUF = decltype(rbuf_c)::value;  // reads: into buffer RBUF,
       constexpr int RST = decltype(rst_c)::value;    //   of stage slot RST,
@@ -526,15 +638,21 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       constexpr int Q0 = decltype(q0_c)::value;      //   loads Q0 ..
       constexpr int NQ = decltype(nq_c)::value;      //   .. Q0 + NQ - 1
       constexpr bool SYNC = decltype(sync_c)::value;
-      constexpr int NIT = NRD + NQ;
+      // the sub-step with the barrier reads the next K-step's first
+      // fragments, and (A8) before them its scales
+      constexpr int NSCS = SYNC ? NSC : 0;
+      constexpr int NRDS = NRD + NSCS;
+      constexpr int NIT = NRDS + NQ;
       auto item = [&](auto m_c) __attribute__((always_inline)) {
         constexpr int m = decltype(m_c)::value;
-        if constexpr (m < NRD)
+        if constexpr (m < NSCS)
+          read_scale(std::integral_constant<int, RST>{}, std::integral_constant<int, m>{});
+        else if constexpr (m < NRDS)
           read_frag(std::integral_constant<int, RBUF>{}, std::integral_constant<int, RST>{},
-                    std::integral_constant<int, RSK>{}, std::integral_constant<int, m>{});
+                    std::integral_constant<int, RSK>{}, std::integral_constant<int, m - NSCS>{});
         else
           issue_load(std::integral_constant<int, LST>{},
-                     std::integral_constant<int, Q0 + m - NRD>{}, soff);
+                     std::integral_constant<int, Q0 + m - NRDS>{}, soff);
       };
       // the barrier of the K-step: this wavefront's reads of the current
       // stage and its loads of the next one are done, then every
@@ -548,12 +666,12 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         constexpr int i = decltype(i_c)::value;
         // items start after row 0 in the sub-step with the barrier
         constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
-        constexpr int ISSUED = BEFORE < NRD ? BEFORE : NRD;
+        constexpr int ISSUED = BEFORE < NRDS ? BEFORE : NRDS;
         wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
+        const bf16x8 av = a_frag(std::integral_constant<int, BUFM>{}, mst_c, i_c);
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUFM][i], fb[BUFM][j], acc[i][j],
-                                                              0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[BUFM][j], acc[i][j], 0, 0, 0);
           if constexpr (!(SYNC && i == 0)) {
             constexpr int m = BEFORE + j;
             if constexpr (m < NIT) item(std::integral_constant<int, m>{});
@@ -577,11 +695,12 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       using N = std::integral_constant<int, NS>;
       const uint32_t s1 = k_offset(kt + 1), s2 = k_offset(kt + 2);
       substep(I0{}, I1{}, S{}, I1{}, N{}, std::integral_constant<int, L3>{},
-              std::integral_constant<int, L0>{}, s1, IF{});
+              std::integral_constant<int, L0>{}, s1, IF{}, S{});
       substep(I1{}, I0{}, S{}, std::integral_constant<int, 2>{}, N{},
-              std::integral_constant<int, L3 + L0>{}, std::integral_constant<int, L1>{}, s1, IF{});
-      substep(I0{}, I1{}, S{}, std::integral_constant<int, 3>{}, N{}, I0{}, I0{}, s1, IF{});
-      substep(I1{}, I0{}, N{}, I0{}, S{}, I0{}, std::integral_constant<int, L3>{}, s2, IT{});
+              std::integral_constant<int, L3 + L0>{}, std::integral_constant<int, L1>{}, s1, IF{},
+              S{});
+      substep(I0{}, I1{}, S{}, std::integral_constant<int, 3>{}, N{}, I0{}, I0{}, s1, IF{}, S{});
+      substep(I1{}, I0{}, N{}, I0{}, S{}, I0{}, std::integral_constant<int, L3>{}, s2, IT{}, S{});
     };
     // the first loads of stage 1 (those sub-step 3 of the step before issues)
     static_for<L3>([&](auto q_c) __attribute__((always_inline)) {
@@ -622,26 +741,35 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       constexpr int SK = decltype(sk_c)::value, r = decltype(r_c)::value;
       if constexpr (r < FN)
         fb[BUF][r] = *((lds_bf16x8_t *)(uintptr_t)fbsk + r * 32 * ROWB / 16);
+      else if constexpr (A8)
+        fa[BUF][r - FN] =
+            *(lds_u32x2_t *)(uintptr_t)(fa_addr[AST][SK] + (r - FN) * WM * 32 * ROWB_A);
       else
         fa[BUF][r - FN] =
             *((lds_bf16x8_t *)(uintptr_t)fa_addr[AST][SK] + (r - FN) * WM * 32 * ROWB / 16);
     };
     auto substep = [&](auto bufm_c, auto rbuf_c, auto rast_c, auto rsk_c, uint32_t rfb,
                        auto las_c, auto q0_c, auto nq_c, int lbs, uint32_t sa, uint32_t sb,
-                       auto sync_c) __attribute__((always_inline)) {
+                       auto sync_c, auto mst_c) __attribute__((always_inline)) {
       constexpr int BUFM = decltype(bufm_c)::value;  // buffer the MFMAs read
       constexpr int RBUF = decltype(rbuf_c)::value;  // reads: into buffer RBUF,
       constexpr int Q0 = decltype(q0_c)::value;      // batch items Q0 ..
       constexpr int NQ = decltype(nq_c)::value;      //   .. Q0 + NQ - 1
       constexpr bool SYNC = decltype(sync_c)::value;
-      constexpr int NIT = NRD + NQ;
+      // the sub-step with the barrier reads the next K-step's first
+      // fragments, and (A8) before them its scales
+      constexpr int NSCS = SYNC ? NSC : 0;
+      constexpr int NRDS = NRD + NSCS;
+      constexpr int NIT = NRDS + NQ;
       auto item = [&](auto m_c) __attribute__((always_inline)) {
         constexpr int m = decltype(m_c)::value;
-        if constexpr (m < NRD)
+        if constexpr (m < NSCS)
+          read_scale(rast_c, std::integral_constant<int, m>{});
+        else if constexpr (m < NRDS)
           read_frag_s(std::integral_constant<int, RBUF>{}, rast_c, rsk_c,
-                      std::integral_constant<int, m>{}, rfb);
+                      std::integral_constant<int, m - NSCS>{}, rfb);
         else
-          batch_item(las_c, std::integral_constant<int, Q0 + m - NRD>{}, lbs, sa, sb);
+          batch_item(las_c, std::integral_constant<int, Q0 + m - NRDS>{}, lbs, sa, sb);
       };
       // the barrier of the K-step: this wavefront's reads of the current
       // slots are done and its loads up to those of kt+1 have landed, then
@@ -654,12 +782,12 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
         constexpr int i = decltype(i_c)::value;
         constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
-        constexpr int ISSUED = BEFORE < NRD ? BEFORE : NRD;
+        constexpr int ISSUED = BEFORE < NRDS ? BEFORE : NRDS;
         wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
+        const bf16x8 av = a_frag(std::integral_constant<int, BUFM>{}, mst_c, i_c);
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[BUFM][i], fb[BUFM][j], acc[i][j],
-                                                              0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[BUFM][j], acc[i][j], 0, 0, 0);
           if constexpr (!(SYNC && i == 0)) {
             constexpr int m = BEFORE + j;
             if constexpr (m < NIT) item(std::integral_constant<int, m>{});
@@ -685,16 +813,16 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
       const uint32_t bo = (uint32_t)bs * B_BYTES, bo1 = (uint32_t)bs1 * B_BYTES;
       // the batch of kt-1 (A of kt+1, B of kt+2) in sub-steps 0 and 1
       substep(I0{}, I1{}, S{}, I1{}, fb_addr[0][1] + bo, N{}, std::integral_constant<int, L3>{},
-              std::integral_constant<int, L0>{}, bs2, s1, s2, IF{});
+              std::integral_constant<int, L0>{}, bs2, s1, s2, IF{}, S{});
       substep(I1{}, I0{}, S{}, std::integral_constant<int, 2>{}, fb_addr[0][2] + bo, N{},
               std::integral_constant<int, L3 + L0>{}, std::integral_constant<int, L1>{}, bs2, s1, s2,
-              IF{});
+              IF{}, S{});
       substep(I0{}, I1{}, S{}, std::integral_constant<int, 3>{}, fb_addr[0][3] + bo, N{}, I0{},
-              I0{}, bs2, s1, s2, IF{});
+              I0{}, bs2, s1, s2, IF{}, S{});
       // barrier; fragments of (kt+1, 0); the first of the batch of kt (A of
       // kt+2 into A slot ST, B of kt+3 into B slot bs)
       substep(I1{}, I0{}, N{}, I0{}, fb_addr[0][0] + bo1, S{}, I0{},
-              std::integral_constant<int, L3>{}, bs, s2, s3, IT{});
+              std::integral_constant<int, L3>{}, bs, s2, s3, IT{}, S{});
     };
     // the first items of the batch of K-step -1: A of 1 (slot 1), B of 2
     // (slot 2)

@@ -203,10 +203,11 @@ int cco_moe_dispatch(cco_moe *m, const uint16_t *x, const float *weights,
  * [H, H + 4 ns) = scales[t] as stored; the rest of the row is not written.
  * DISP_META as for cco_moe_dispatch.  Needs the same T and idx as the
  * preceding plan.  Moves half the token bytes of the bf16 dispatch.
- * Until the next cco_moe_dispatch, the bf16 SwiGLU (cco_moe_expert) and a
- * combine of identity experts through the receive window refuse to read
- * these rows (CCO_ERR_INVALID_ARG): the caller's own expert reads
- * cco_moe_dispatch_view and writes cco_moe_combine_in_view.
+ * Until the next cco_moe_dispatch, cco_moe_expert reads these rows as OCP
+ * e4m3 values with fp32 block scales (see there), and a combine of identity
+ * experts through the receive window refuses them (CCO_ERR_INVALID_ARG); a
+ * caller's own expert reads cco_moe_dispatch_view and writes
+ * cco_moe_combine_in_view.
  * Errors: CCO_ERR_INVALID_ARG for the checks above, before any launch. */
 int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int32_t ns,
                          const float *weights, int32_t T, void *stream);
@@ -223,7 +224,20 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
  * device; nothing is copied to the host.  Results are deterministic for a
  * given routing on a given device: in GEMMs of few tile rounds the last
  * tiles sum their K-steps in ranges, added in range order.  With
- * inter == 0 this is a no-op (identity experts; w13 and w2 may be NULL). */
+ * inter == 0 this is a no-op (identity experts; w13 and w2 may be NULL).
+ * After cco_moe_dispatch_fp8 the rows X are the 8-bit receive rows, read in
+ * place ([blog] "Zero-copy MoE dispatch", step 1: the received tokens come
+ * with their scales; that the expert applies them as below is this
+ * library's reading, the page leaves it open): byte k of a row is an OCP
+ * e4m3fn code (1 sign, 4 exponent bits of bias 7, 3 mantissa bits; no
+ * infinities, S.1111.111 is NaN), and value k of the row is
+ *   X[k] = bf16( binary32(e4m3(code k) * scale[k / (H / ns)]) )
+ * with the ns fp32 scales after the H codes (scale 1 when ns == 0): each
+ * product rounded to nearest even in binary32, then to bf16.  The GEMMs
+ * then run as for bf16 rows, so the results equal the bf16 path's on
+ * those X bit for bit.  H / ns must be 64 times a power of two (the scale
+ * blocks are whole runs of the GEMM's 64-value K-steps), else
+ * CCO_ERR_INVALID_ARG before any launch. */
 int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *stream);
 
 /* Receive window of `slot` ([blog] "Zero-copy MoE dispatch -> expert ->

@@ -36,7 +36,8 @@ hipError_t launch_combine(const MoeArgs &, uint64_t, const float *, const int32_
 hipError_t launch_copy_in(const MoeArgs &, int32_t, const uint16_t *, uint64_t, hipStream_t) {
   return hipErrorInvalidValue;
 }
-hipError_t launch_expert_gate_up(const MoeArgs &, const uint16_t *, int32_t, int, hipStream_t) {
+hipError_t launch_expert_gate_up(const MoeArgs &, const uint16_t *, int32_t, int, int32_t,
+                                 hipStream_t) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_expert_down(const MoeArgs &, const uint16_t *, int32_t, int, hipStream_t) {

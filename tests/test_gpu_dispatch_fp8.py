@@ -150,34 +150,31 @@ def test_dispatch_fp8_empty_batch_and_rejections(ccm):
     heap8.destroy()
 
 
-def test_bf16_readers_refuse_8bit_rows(ccm):
-    cfg = get_config("tiny")
-    heap, moe = make_moe(cfg)
+def test_identity_combine_refuses_8bit_rows(ccm):
+    # identity experts: combine would read the 8-bit rows through the view
+    # as bf16; the caller's own expert output (a foreign pointer) is fine,
+    # and a bf16 dispatch makes the rows bf16 again.  (The SwiGLU expert
+    # reads 8-bit rows as such: tests/test_gpu_expert_fp8.py.)
+    cfg = get_config("tiny").with_(I=0)
     x8, sc, idx, w = _inputs(cfg, 128)
-    from synth.gen import expert_weights
-    w13, w2 = expert_weights(cfg, "cuda")
+    heap, moe = make_moe(cfg)
     moe.plan(_dev(idx))
     moe.dispatch_fp8(_dev(x8), _dev(sc), _dev(w))
     with pytest.raises(ccm.CcoError):
-        moe.expert(w13, w2)
-    # the caller's own expert writes the staging view; combine reads it
-    out, code = moe.combine(_dev(w))
-    assert code == ccm.CCO_OK
-    # a bf16 dispatch makes the rows bf16 again
+        moe.combine(_dev(w))
+    tot = moe.read_routing()[3]
+    own = [torch.zeros((max(int(tot[s]), 1), cfg.H), dtype=torch.bfloat16, device="cuda")
+           for s in range(cfg.S)]
+    out, code = moe.combine(_dev(w), expert_out=own)
+    assert code == ccm.CCO_INFO_COPIED
+    torch.cuda.synchronize()
+    assert not out.float().abs().sum().item()
     xb = torch.randn(cfg.T, cfg.H).to(torch.bfloat16).cuda()
     moe.dispatch(xb, _dev(w))
-    moe.expert(w13, w2)
+    out, code = moe.combine(_dev(w))
     torch.cuda.synchronize()
+    assert code == ccm.CCO_OK
     heap.destroy()
-    # identity experts: combine would read the 8-bit rows through the view
-    cfgi = cfg.with_(I=0)
-    heapi, moei = make_moe(cfgi)
-    moei.plan(_dev(idx))
-    moei.dispatch_fp8(_dev(x8), _dev(sc), _dev(w))
-    with pytest.raises(ccm.CcoError):
-        moei.combine(_dev(w))
-    torch.cuda.synchronize()
-    heapi.destroy()
 
 
 def test_dispatch_fp8_dsv3_full_sampled(ccm, orc):
