@@ -165,6 +165,15 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 q, float s) {
   return r;
 }
 
+// Values 2Q, 2Q + 1 of the same conversion, into r (a quarter of the
+// fragment, so that the work can be spread between MFMAs).
+template <int Q>
+__device__ __forceinline__ void e4m3x2_to_bf16(bf16x8 &r, u32x2 q, float s) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)(Q < 2 ? q.x : q.y), (Q & 1) != 0);
+  r[2 * Q] = (__bf16)(f.x * s);
+  r[2 * Q + 1] = (__bf16)(f.y * s);
+}
+
 // LDS tile layout: rows of BK bf16 (ROWB bytes), unpadded, 16-byte chunks
 // XOR-swizzled per row so that the 16 rows one fragment read touches fall
 // on distinct bank groups: physical chunk = logical chunk ^ swz(row).
@@ -505,14 +514,51 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         sc[ST][i] = unit_scale ? 1.0f : v;
       }
     };
-    // the bf16 A fragment of row i of the MFMAs: buffer BUFM, K-step of A slot MST
-    auto a_frag = [&](auto bufm_c, auto mst_c, auto i_c) __attribute__((always_inline)) {
+    // The MFMAs of a sub-step (K-steps of 64): NACT rows of FN MFMAs from
+    // fragment buffer BUFM (A of slot MST), one item after each MFMA; with
+    // SYNC the items start after row 0 and the barrier.  Before row i a
+    // progressive lgkmcnt wait lets the row start as soon as its A fragment
+    // (and the B fragments read before it) are in.  8-bit A: the fragment of
+    // row i + 1 is converted during the MFMAs of row i, a quarter after each
+    // (its wait moves up one row), so that only row 0's conversion stands
+    // between the LDS reads and the matrix cores.
+    auto mfma_rows = [&](auto bufm_c, auto mst_c, auto sync_c, auto nrds_c, auto nit_c,
+                         auto &&item, auto &&sync) __attribute__((always_inline)) {
       constexpr int BUFM = decltype(bufm_c)::value, MST = decltype(mst_c)::value;
-      constexpr int i = decltype(i_c)::value;
-      if constexpr (A8)
-        return e4m3x8_to_bf16(fa[BUFM][i], sc[MST][i]);
-      else
-        return fa[BUFM][i];
+      constexpr bool SYNC = decltype(sync_c)::value;
+      constexpr int NRDS = decltype(nrds_c)::value, NIT = decltype(nit_c)::value;
+      [[maybe_unused]] bf16x8 cva[NF];
+      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
+        constexpr int ISSUED = BEFORE < NRDS ? BEFORE : NRDS;
+        constexpr int NEED = (A8 && i + 1 < NACT) ? i + 1 : i;  // last A fragment needed
+        wait_lgkmcnt<(NACT - 1 - NEED) + ISSUED>();
+        bf16x8 av;
+        if constexpr (A8) {
+          if constexpr (i == 0) cva[0] = e4m3x8_to_bf16(fa[BUFM][0], sc[MST][0]);
+          av = cva[i];
+        } else {
+          av = fa[BUFM][i];
+        }
+        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[BUFM][j], acc[i][j], 0, 0, 0);
+          if constexpr (!(SYNC && i == 0)) {
+            constexpr int m = BEFORE + j;
+            if constexpr (m < NIT) item(std::integral_constant<int, m>{});
+          }
+          if constexpr (A8 && i + 1 < NACT)
+            e4m3x2_to_bf16<j>(cva[i + 1], fa[BUFM][i + 1], sc[MST][i + 1]);
+        });
+        if constexpr (SYNC && i == 0) sync();
+      });
+      if constexpr (SYNC && NACT == 0) sync();
+      // items the MFMAs did not cover (few active rows)
+      constexpr int COVERED = NACT == 0 ? 0 : (SYNC ? (NACT - 1) * FN : NACT * FN);
+      static_for<(NIT > COVERED) ? NIT - COVERED : 0>([&](auto t_c) __attribute__((always_inline)) {
+        item(std::integral_constant<int, COVERED + decltype(t_c)::value>{});
+      });
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -630,7 +676,6 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     auto substep = [&](auto bufm_c, auto rbuf_c, auto rst_c, auto rsk_c, auto lst_c, auto q0_c,
                        auto nq_c, uint32_t soff, auto sync_c, auto mst_c)
                        __attribute__((always_inline)) {
-      constexpr int BUFM = decltype(bufm_c)::value;  // buffer the MFMAs read
       constexpr int RBUF = decltype(rbuf_c)::value;  // reads: into buffer RBUF,
       constexpr int RST = decltype(rst_c)::value;    //   of stage slot RST,
       constexpr int RSK = decltype(rsk_c)::value;    //   sub-step RSK
@@ -662,29 +707,8 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         wait_vmcnt<0>();
         stage_barrier();
       };
-      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
-        constexpr int i = decltype(i_c)::value;
-        // items start after row 0 in the sub-step with the barrier
-        constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
-        constexpr int ISSUED = BEFORE < NRDS ? BEFORE : NRDS;
-        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
-        const bf16x8 av = a_frag(std::integral_constant<int, BUFM>{}, mst_c, i_c);
-        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-          constexpr int j = decltype(j_c)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[BUFM][j], acc[i][j], 0, 0, 0);
-          if constexpr (!(SYNC && i == 0)) {
-            constexpr int m = BEFORE + j;
-            if constexpr (m < NIT) item(std::integral_constant<int, m>{});
-          }
-        });
-        if constexpr (SYNC && i == 0) sync();
-      });
-      if constexpr (SYNC && NACT == 0) sync();
-      // items the MFMAs did not cover (few active rows)
-      constexpr int COVERED = NACT == 0 ? 0 : (SYNC ? (NACT - 1) * FN : NACT * FN);
-      static_for<(NIT > COVERED) ? NIT - COVERED : 0>([&](auto t_c) __attribute__((always_inline)) {
-        item(std::integral_constant<int, COVERED + decltype(t_c)::value>{});
-      });
+      mfma_rows(bufm_c, mst_c, sync_c, std::integral_constant<int, NRDS>{},
+                std::integral_constant<int, NIT>{}, item, sync);
     };
     using IT = std::true_type;
     using IF = std::false_type;
@@ -751,7 +775,6 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     auto substep = [&](auto bufm_c, auto rbuf_c, auto rast_c, auto rsk_c, uint32_t rfb,
                        auto las_c, auto q0_c, auto nq_c, int lbs, uint32_t sa, uint32_t sb,
                        auto sync_c, auto mst_c) __attribute__((always_inline)) {
-      constexpr int BUFM = decltype(bufm_c)::value;  // buffer the MFMAs read
       constexpr int RBUF = decltype(rbuf_c)::value;  // reads: into buffer RBUF,
       constexpr int Q0 = decltype(q0_c)::value;      // batch items Q0 ..
       constexpr int NQ = decltype(nq_c)::value;      //   .. Q0 + NQ - 1
@@ -779,27 +802,8 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         wait_vmcnt<LB>();
         stage_barrier();
       };
-      static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
-        constexpr int i = decltype(i_c)::value;
-        constexpr int BEFORE = SYNC ? (i == 0 ? 0 : (i - 1) * FN) : i * FN;
-        constexpr int ISSUED = BEFORE < NRDS ? BEFORE : NRDS;
-        wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
-        const bf16x8 av = a_frag(std::integral_constant<int, BUFM>{}, mst_c, i_c);
-        static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
-          constexpr int j = decltype(j_c)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[BUFM][j], acc[i][j], 0, 0, 0);
-          if constexpr (!(SYNC && i == 0)) {
-            constexpr int m = BEFORE + j;
-            if constexpr (m < NIT) item(std::integral_constant<int, m>{});
-          }
-        });
-        if constexpr (SYNC && i == 0) sync();
-      });
-      if constexpr (SYNC && NACT == 0) sync();
-      constexpr int COVERED = NACT == 0 ? 0 : (SYNC ? (NACT - 1) * FN : NACT * FN);
-      static_for<(NIT > COVERED) ? NIT - COVERED : 0>([&](auto t_c) __attribute__((always_inline)) {
-        item(std::integral_constant<int, COVERED + decltype(t_c)::value>{});
-      });
+      mfma_rows(bufm_c, mst_c, sync_c, std::integral_constant<int, NRDS>{},
+                std::integral_constant<int, NIT>{}, item, sync);
     };
     using IT = std::true_type;
     using IF = std::false_type;
