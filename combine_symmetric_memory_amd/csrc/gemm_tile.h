@@ -543,7 +543,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         }
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[BUFM][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[BUFM][j], av, acc[i][j], 0, 0, 0);
           if constexpr (!(SYNC && i == 0)) {
             constexpr int m = BEFORE + j;
             if constexpr (m < NIT) item(std::integral_constant<int, m>{});
@@ -610,7 +610,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value, m = i * FN + j;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
           if constexpr (m < NRD) read_frag(I1{}, st_c, I1{}, std::integral_constant<int, m>{});
           else if constexpr (m - NRD < H0)
             issue_load(std::integral_constant<int, LST>{}, std::integral_constant<int, m - NRD>{}, soff);
@@ -640,7 +640,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
         wait_lgkmcnt<(NACT - 1 - i) + ISSUED>();
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value, m = (i - 1) * FN + j;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[1][j], fa[1][i], acc[i][j], 0, 0, 0);
           if constexpr (i >= 1) {
             if constexpr (m < NRD) read_frag(I0{}, std::integral_constant<int, NST>{}, I0{}, std::integral_constant<int, m>{});
             else if constexpr (m - NRD < H1)
@@ -850,64 +850,79 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     // every wavefront is done with the LDS before the next tile refills it
     __syncthreads();
 
+    // The MFMAs take the weights as their first operand, so each 32x32
+    // block holds the tile transposed: lane holds output row (lane % 32) of
+    // the block and, for accumulator element v, output column
+    // 8 * (v / 4) + 4 * (lane / 32) + v % 4 -- runs of four consecutive
+    // columns of one row.
     if (part != nullptr) {
-      // partial sums of a K-range: straight from the accumulators, 32
-      // consecutive floats of two rows per store
+      // partial sums of a K-range: straight from the accumulators, four
+      // consecutive floats of a row per store
       static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
         constexpr int i = decltype(i_c)::value;
-        const int rb = (wm + i * WM) * 32 + (lane / 32) * 4;
+        const int row = (wm + i * WM) * 32 + (lane & 31);
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
           asm volatile("" : "+a"(acc[i][j]));
-          const int col = wn * TN + j * 32 + (lane & 31);
+          float *prow = part + row * BN + wn * TN + j * 32 + (lane / 32) * 4;
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            part[(rb + (v / 4) * 8 + (v % 4)) * BN + col] = acc[i][j][v];
+          for (int q = 0; q < 4; ++q)
+            *(float4 *)(prow + q * 8) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                    acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         });
       });
       return;
     }
 
     // Epilogue, through the (now idle) ring: the wavefronts write the tile,
-    // rounded to bf16, row-major into LDS; then all threads copy the rows
-    // that exist to the staging window in 16-byte pieces.  Rows carry 16
-    // bytes of padding, so the two half-wavefronts of one LDS write (rows r
-    // and r + 4) land on different banks.
-    // In a 32x32 block, lane holds column (lane % 32), rows
-    // 8 * (v / 4) + 4 * (lane / 32) + v % 4 for accumulator element v.  The
-    // empty asm statements pin each block's accumulator reads after the
-    // previous block's LDS writes, which keeps the compiler from hoisting
-    // every accumulator into VGPRs at once.
+    // rounded to bf16, row-major into LDS, four columns (8 bytes) per write;
+    // then all threads copy the rows that exist to the staging window in
+    // 16-byte pieces.  Rows carry 16 bytes of padding (they stay 16-byte
+    // aligned for the copy), so the 32 rows one half-wavefront writes fall
+    // on at most two rows of banks.  The empty asm
+    // statements pin each block's accumulator reads after the previous
+    // block's LDS writes, which keeps the compiler from hoisting every
+    // accumulator into VGPRs at once.
     constexpr int OUT_COLS = SWIGLU ? BN / 2 : BN;
     constexpr int OROWB = OUT_COLS * 2 + 16;
     static_assert(BM * OROWB <= kGemmLdsBytes, "the output tile must fit the LDS");
-    typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+    typedef __attribute__((address_space(3))) u32x2 lds_w_u32x2_t;
     typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
     lds_char_t *otile = (lds_char_t *)smem;
+    auto pack2 = [](float lo, float hi) __attribute__((always_inline)) {
+      return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+    };
     static_for<NACT>([&](auto i_c) __attribute__((always_inline)) {
       constexpr int i = decltype(i_c)::value;
-      const int rb = (wm + i * WM) * 32 + (lane / 32) * 4;
+      lds_char_t *orow = otile + ((wm + i * WM) * 32 + (lane & 31)) * OROWB + (lane / 32) * 8;
       if constexpr (SWIGLU) {
         static_for<FN / 2>([&](auto p_c) __attribute__((always_inline)) {
           constexpr int p = decltype(p_c)::value;
           asm volatile("" : "+a"(acc[i][2 * p]), "+a"(acc[i][2 * p + 1]));
-          const int col = wn * (TN / 2) + p * 32 + (lane & 31);
+          const int col = wn * (TN / 2) + p * 32;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = rb + (v / 4) * 8 + (v % 4);
-            const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
-            *((lds_u16_t *)(otile + row * OROWB) + col) = f32_to_bf16_rne(h);
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              h[c] = silu(acc[i][2 * p][4 * q + c]) * acc[i][2 * p + 1][4 * q + c];
+            u32x2 w2;
+            w2.x = pack2(h[0], h[1]);
+            w2.y = pack2(h[2], h[3]);
+            *(lds_w_u32x2_t *)(orow + (col + q * 8) * 2) = w2;
           }
         });
       } else {
         static_for<FN>([&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
           asm volatile("" : "+a"(acc[i][j]));
-          const int col = wn * TN + j * 32 + (lane & 31);
+          const int col = wn * TN + j * 32;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = rb + (v / 4) * 8 + (v % 4);
-            *((lds_u16_t *)(otile + row * OROWB) + col) = f32_to_bf16_rne(acc[i][j][v]);
+          for (int q = 0; q < 4; ++q) {
+            u32x2 w2;
+            w2.x = pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            w2.y = pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *(lds_w_u32x2_t *)(orow + (col + q * 8) * 2) = w2;
           }
         });
       }
