@@ -7,8 +7,8 @@ on oracle.dequant_e4m3_rows of the GPU's own receive rows, combine bit-exact
 on the GPU's own expert rows.  Against the bf16 path: a bf16 dispatch of the
 oracle's dequantized tokens gives bit-identical HBUF, expert rows and
 combine output (same tiles, same K order, same bf16 operands).  Scale blocks
-of 1, 2, 4 and 8 K-steps, no scales, half tiles and split K-ranges, ragged
-and empty batches, the full DeepSeek-V3 shape, and the host-side
+of 1, 2, 4, 8 and 16 K-steps, no scales, half tiles and split K-ranges, ragged
+and empty batches, the full DeepSeek-V3 and Mixtral shapes, and the host-side
 rejections."""
 import gc
 from concurrent.futures import ThreadPoolExecutor
@@ -230,6 +230,50 @@ def test_expert_8bit_dsv3_full_size(ccm, orc):
         # the expert's first and last row, through the oracle's SwiGLU
         s, o, c = int(e) // cfg.eps, int(ref.expert_off[e]), int(ref.counts[e])
         rows = sorted({0, c - 1})
+        X = np.concatenate([orc.dequant_e4m3_rows(_read_rows8(moe, s, o + r, 1), ns)
+                            for r in rows])
+        Y = np.stack([moe.read_rows("out_tok", s, o + r, 1)[0] for r in rows])
+        return Y, orc.swiglu_rows(X, w13h[e], w2h[e], nthreads=2)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(one, [int(e) for e in np.nonzero(ref.counts)[0]]))
+    Y = np.concatenate([r[0] for r in res])
+    say("  %d experts, %d sampled rows" % (len(res), len(Y)))
+    assert_close(Y, np.concatenate([r[1] for r in res]), "expert rows (sampled)")
+    ot8 = [moe.read_rows("out_tok", s, 0, int(tot[s])) for s in range(cfg.S)]
+    xb = torch.from_numpy(orc.dequant_e4m3_rows(_token_rows(x8, sc), ns).view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    outb, code = _run_bf16(moe, xb, idx, w, w13, w2)
+    assert code == ccm.CCO_OK
+    for s in range(cfg.S):
+        np.testing.assert_array_equal(ot8[s], moe.read_rows("out_tok", s, 0, int(tot[s])),
+                                      err_msg="expert rows slot %d" % s)
+    assert torch.equal(out8.view(torch.int16), outb.view(torch.int16))
+    say("  whole path bit-identical to the bf16 path")
+    heap.destroy()
+
+
+def test_expert_8bit_mixtral_full_size(ccm, orc):
+    # the full Mixtral shape (T = 4096, H = 4096, top-2 of 8 experts, one per
+    # slot, I = 14336; gate/up bound by the matrix cores, down split into
+    # K-ranges in its last round): one row of every 256-row m-tile of every
+    # expert against the oracle, and the whole path bit-identical to the bf16
+    # path on the oracle's dequantized tokens
+    cfg = get_config("mixtral")
+    say("case: 8-bit expert mixtral full size")
+    x8, sc, idx, w = _inputs(cfg, 128)
+    ns = sc.shape[1]
+    heap, moe = make_moe(cfg)
+    w13, w2 = expert_weights(cfg, "cuda")
+    out8, code = _run_fp8(moe, x8, sc, idx, w, w13, w2)
+    assert code == ccm.CCO_OK and moe.status()[0] == ccm.CCO_OK
+    ref = orc.plan(idx, cfg.E, cfg.S, moe.cap)
+    tot = moe.read_routing()[3]
+    w13h, w2h = bf16_bits(w13), bf16_bits(w2)
+
+    def one(e):
+        s, o, c = e // cfg.eps, int(ref.expert_off[e]), int(ref.counts[e])
+        rows = sorted({min(c - 1, m + (7 * m // 256) % 256) for m in range(0, c, 256)} | {c - 1})
         X = np.concatenate([orc.dequant_e4m3_rows(_read_rows8(moe, s, o + r, 1), ns)
                             for r in rows])
         Y = np.stack([moe.read_rows("out_tok", s, o + r, 1)[0] for r in rows])
