@@ -34,7 +34,7 @@ namespace {
 // Persistent grouped GEMM over every expert's tiles.  List order inside an
 // expert: n-tile major, m-tile minor, so the m-tiles of one weight panel run
 // side by side; with a half remainder, the pair of column tiles (2j, 2j+1)
-// lists its full m-tiles and then the remainder tile j that spans both.
+// lists the remainder tile j that spans both and then its full m-tiles.
 // TAIL = false runs the whole tiles; TAIL = true, launched after it, the
 // K-ranges of the split tiles (each instantiation keeps only its own
 // epilogue, so the main one's register allocation is not disturbed).

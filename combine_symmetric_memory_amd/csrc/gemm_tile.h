@@ -966,15 +966,19 @@ __device__ __forceinline__ ExpertTiles expert_tiles(int rows, int ntl) {
 
 // Tile r (0 <= r < units) of an expert with `rows` rows, in list order:
 // n-tile major, m-tile minor; with a half remainder, the column-tile pair
-// (2j, 2j+1) lists its full m-tiles and then the remainder tile j that spans
-// both (kind 2: 128 rows x 2 BN; kind 1: BM x BN).
+// (2j, 2j+1) lists the remainder tile j that spans both (kind 2: 128 rows x
+// 2 BN) and then its full m-tiles (kind 1: BM x BN).  The remainder tile
+// streams both weight panels with one K-step in flight and is the slowest
+// tile of the group: started first, it leads, and the full tiles started
+// after it catch up and read its panels from L2 (listed last, it fell
+// behind and read them again).
 struct TileRef {
   int kind, n_tile, m_tile, row0, rows_valid;
 };
 
 __device__ __forceinline__ TileRef decode_tile(const ExpertTiles &et, int r, int rows) {
   TileRef t;
-  if (et.half && r % (2 * et.q + 1) == 2 * et.q) {
+  if (et.half && r % (2 * et.q + 1) == 0) {
     t.kind = 2;
     t.n_tile = r / (2 * et.q + 1);
     t.m_tile = et.q;
@@ -984,7 +988,7 @@ __device__ __forceinline__ TileRef decode_tile(const ExpertTiles &et, int r, int
     if (et.half) {
       const int per = 2 * et.q + 1;
       const int j = r / per;
-      const int rr = r - j * per;
+      const int rr = r - j * per - 1;
       t.n_tile = 2 * j + rr / et.q;
       t.m_tile = rr % et.q;
     } else {
