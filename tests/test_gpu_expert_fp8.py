@@ -8,8 +8,8 @@ on the GPU's own expert rows.  Against the bf16 path: a bf16 dispatch of the
 oracle's dequantized tokens gives bit-identical HBUF, expert rows and
 combine output (same tiles, same K order, same bf16 operands).  Scale blocks
 of 1, 2, 4, 8 and 16 K-steps, no scales, half tiles and split K-ranges, ragged
-and empty batches, the full DeepSeek-V3 and Mixtral shapes, and the host-side
-rejections."""
+and empty batches, eleven seeded random shapes, the full DeepSeek-V3 and
+Mixtral shapes, and the host-side rejections."""
 import gc
 from concurrent.futures import ThreadPoolExecutor
 
@@ -102,16 +102,11 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,over,block,T,scaled", CASES)
-def test_expert_8bit_matches_oracle(ccm, orc, name, over, block, T, scaled):
-    cfg = get_config("tiny").with_(name=name, **over)
-    say("case: 8-bit expert vs oracle", name, cfg, "block", block, "T", T, "scaled", scaled)
-    x8, sc, idx, w = _inputs(cfg, block, T, scaled)
+def _check_against_oracle(ccm, orc, cfg, moe, x8, sc, idx, w, w13, w2, out):
+    """Receive rows and positions bit-exact; every expert's rows within
+    tolerance of the oracle's SwiGLU on the dequantized GPU receive rows;
+    combine bit-exact on the GPU's own expert rows."""
     ns = 0 if sc is None else sc.shape[1]
-    heap, moe = make_moe(cfg)
-    w13, w2 = expert_weights(cfg, "cuda")
-    out, code = _run_fp8(moe, x8, sc, idx, w, w13, w2)
-    assert code == ccm.CCO_OK and moe.status()[0] == ccm.CCO_OK
     E, S, cap = cfg.E, cfg.S, moe.cap
     ref = orc.plan(idx, E, S, cap)
     pos, counts, off, tot = moe.read_routing()
@@ -135,6 +130,18 @@ def test_expert_8bit_matches_oracle(ccm, orc, name, over, block, T, scaled):
                          "expert %d (%d rows)" % (e, c))
     np.testing.assert_array_equal(bf16_bits(out),
                                   orc.combine_tokens(full, w, idx, ref.pos, E, S))
+
+
+@pytest.mark.parametrize("name,over,block,T,scaled", CASES)
+def test_expert_8bit_matches_oracle(ccm, orc, name, over, block, T, scaled):
+    cfg = get_config("tiny").with_(name=name, **over)
+    say("case: 8-bit expert vs oracle", name, cfg, "block", block, "T", T, "scaled", scaled)
+    x8, sc, idx, w = _inputs(cfg, block, T, scaled)
+    heap, moe = make_moe(cfg)
+    w13, w2 = expert_weights(cfg, "cuda")
+    out, code = _run_fp8(moe, x8, sc, idx, w, w13, w2)
+    assert code == ccm.CCO_OK and moe.status()[0] == ccm.CCO_OK
+    _check_against_oracle(ccm, orc, cfg, moe, x8, sc, idx, w, w13, w2, out)
     heap.destroy()
 
 
@@ -170,6 +177,52 @@ def test_expert_8bit_is_the_bf16_path_on_dequantized_tokens(ccm, orc, name, over
     # only after an 8-bit dispatch
     again, _ = _run_fp8(moe, x8, sc, idx, w, w13, w2)
     assert torch.equal(again.view(torch.int16), out8.view(torch.int16))
+    heap.destroy()
+
+
+def _random_8bit_shapes(n=10, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        S = int(rng.choice([1, 2, 4, 8]))
+        E = S * int(rng.integers(1, 9))
+        K = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        H = 256 * int(rng.integers(1, 9))
+        I = 128 * int(rng.integers(1, 5))
+        T = int(rng.choice([1, 7, 64, 257, 600]))
+        blocks = [b for b in (64, 128, 256, 512, 1024, 2048) if H % b == 0]
+        block = int(rng.choice(blocks))
+        scaled = rng.random() < 0.85
+        if K > E or T * K > 5000:
+            continue
+        out.append((H, I, E, S, K, T, block, scaled))
+    return out
+
+
+@pytest.mark.parametrize("H,I,E,S,K,T,block,scaled",
+                         _random_8bit_shapes() + [(512, 256, 8, 2, 2, 300, 128, False)])
+def test_expert_8bit_random_shape(ccm, orc, H, I, E, S, K, T, block, scaled):
+    cfg = get_config("tiny").with_(name="random8", H=H, I=I, E=E, S=S, K=K, T=T)
+    say("case: 8-bit random H=%d I=%d E=%d S=%d K=%d T=%d block=%d scaled=%s" %
+        (H, I, E, S, K, T, block, scaled))
+    x8, sc, idx, w = _inputs(cfg, block, T, scaled)
+    ns = 0 if sc is None else sc.shape[1]
+    heap, moe = make_moe(cfg)
+    w13, w2 = expert_weights(cfg, "cuda")
+    out8, code = _run_fp8(moe, x8, sc, idx, w, w13, w2)
+    assert code == ccm.CCO_OK and moe.status()[0] == ccm.CCO_OK
+    _check_against_oracle(ccm, orc, cfg, moe, x8, sc, idx, w, w13, w2, out8)
+    tot = moe.read_routing()[3]
+    hb8, ot8 = _windows(moe, tot)
+    xb = torch.from_numpy(orc.dequant_e4m3_rows(_token_rows(x8, sc), ns).view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    outb, code = _run_bf16(moe, xb, idx, w, w13, w2)
+    assert code == ccm.CCO_OK
+    hbb, otb = _windows(moe, tot)
+    for s in range(S):
+        np.testing.assert_array_equal(hb8[s], hbb[s], err_msg="HBUF slot %d" % s)
+        np.testing.assert_array_equal(ot8[s], otb[s], err_msg="expert rows slot %d" % s)
+    assert torch.equal(out8.view(torch.int16), outb.view(torch.int16))
     heap.destroy()
 
 
