@@ -10,7 +10,7 @@ whole-step throughput (tokens/s), per-kernel times from HIP events on the
 launch stream, the roofline of the dominant kernel and the CPU oracle timed
 on a bounded sample of the same workload.
 
-This build runs on one GPU: --gpus above 1 exits with a message.
+The path runs on one GPU: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
@@ -415,7 +415,7 @@ def main():
                          "(reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU's share of the path; "
+        print("bench.py: the path runs on one GPU (its share of the work); "
               "--gpus %d is not supported (use --gpus 1)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
