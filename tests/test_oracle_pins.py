@@ -602,8 +602,10 @@ def _dequant_witnesses(seed: int = 7):
 def test_dequant_rounds_the_scaled_value_twice_to_nearest_even():
     """Decoded value times its block's scale, rounded to binary32 and then to
     bf16 (both to nearest even): against exact rationals on random codes and
-    scales, on exact binary32 ties, on exact bf16 ties, and on cases where
-    one rounding of the exact product would give another bf16."""
+    scales (each value with its block's scale, ns = 1, 2, 4), and on
+    constructed codes and scales whose product is an exact binary32 tie, an
+    exact bf16 tie, or a value one rounding of which would give another
+    bf16."""
     from oracle import oracle as orc
     vals = _e4m3_codes_f32()
     f32_ties, bf16_ties, double = _dequant_witnesses()
@@ -614,10 +616,6 @@ def test_dequant_rounds_the_scaled_value_twice_to_nearest_even():
         H = 256
         q = rng.choice(finite, size=(3, H)).astype(np.uint8)
         sc = (rng.uniform(0.5, 2.0, (3, ns)) * 2.0 ** rng.integers(-12, 12, (3, ns))).astype(np.float32)
-        # plant the witnesses at the start of row 0 (their scale is block 0's)
-        wit = f32_ties + bf16_ties + double
-        for i, (c, s) in enumerate(wit[:min(len(wit), H // ns)]):
-            q[0, i] = c
         got = orc.dequant_e4m3_rows(_rows_8bit(q, sc), ns)
         blk = H // ns
         for r in range(3):
