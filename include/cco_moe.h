@@ -243,9 +243,11 @@ int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *st
 /* Receive window of `slot` ([blog] "Zero-copy MoE dispatch -> expert ->
  * combine", step 1: the received tokens the op's dispatch returns are not a
  * new tensor but a view of the "disp_out" region of symmetric memory, which
- * the dispatching peers wrote directly): DISP_X base, [cap][H] bf16; rows
- * [expert_off[e], expert_off[e] + counts[e]) belong to expert e, and the
- * first slot_total[slot] rows are the ones received.  Borrowed: valid until
+ * the dispatching peers wrote directly): DISP_X base, [cap][H] bf16 (after
+ * cco_moe_dispatch_fp8: the same 2H-byte rows holding the 8-bit codes and
+ * their scales, see there); rows [expert_off[e], expert_off[e] + counts[e])
+ * belong to expert e, and the first slot_total[slot] rows are the ones
+ * received.  Borrowed: valid until
  * the heap is destroyed, overwritten by the next dispatch.  NULL if slot is
  * out of range or m is NULL. */
 void *cco_moe_dispatch_view(cco_moe *m, int32_t slot);
