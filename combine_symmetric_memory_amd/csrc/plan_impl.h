@@ -106,25 +106,38 @@ __device__ __forceinline__ bool plan_count_chunk(const MoeArgs &a, const int32_t
   if (!is_last) return false;
   __threadfence();
 
-  // per expert: total over chunks, and each chunk's exclusive prefix; the
-  // chunks' counts are loaded kBatch at a time, so the loads of a batch are
-  // in flight together rather than one after another
-  constexpr int kBatch = 16;
-  for (int e = tid; e <= E; e += kPlanThreads) {
-    int32_t run = 0;
+  // per expert: total over chunks, and each chunk's exclusive prefix.  A
+  // thread takes two of the E + 1 columns at a time (with 256 experts the
+  // thread that owns expert 0 also owns the invalid-id column), and the
+  // chunks' counts of both are loaded kBatch at a time, so that the loads
+  // of a batch are in flight together rather than one after another
+  constexpr int kBatch = 32;
+  for (int e0 = tid; e0 <= E; e0 += 2 * kPlanThreads) {
+    const int e1 = e0 + kPlanThreads;
+    const bool two = e1 <= E;
+    int32_t run0 = 0, run1 = 0;
     for (int b0 = 0; b0 < nblk; b0 += kBatch) {
-      int32_t v[kBatch];
+      int32_t v0[kBatch], v1[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        v[i] = (b0 + i < nblk) ? a.hist[(int64_t)(b0 + i) * (E + 1) + e] : 0;
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t row = (int64_t)(b0 + i) * (E + 1);
+        v0[i] = (b0 + i < nblk) ? a.hist[row + e0] : 0;
+        v1[i] = (two && b0 + i < nblk) ? a.hist[row + e1] : 0;
+      }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         if (b0 + i < nblk) {
-          a.hist[(int64_t)(b0 + i) * (E + 1) + e] = run;
-          run += v[i];
+          const int64_t row = (int64_t)(b0 + i) * (E + 1);
+          a.hist[row + e0] = run0;
+          run0 += v0[i];
+          if (two) {
+            a.hist[row + e1] = run1;
+            run1 += v1[i];
+          }
         }
     }
-    lh[e] = run;
+    lh[e0] = run0;
+    if (two) lh[e1] = run1;
   }
   __syncthreads();
   const int32_t bad_total = lh[E];
@@ -164,6 +177,17 @@ __device__ __forceinline__ void plan_rank_chunk(const MoeArgs &a, const int32_t 
   int32_t *run = lds;          // [E]: next row of each expert for this chunk
   int32_t *wcnt = lds + E;     // [kPlanWaves][E]: pairs per expert in each wave this round
 
+  // this thread's ids of every round (E marks an invalid pair or none),
+  // loaded before the offsets so that all of these loads are in flight at
+  // once
+  const int64_t base = (int64_t)chunk * kPlanChunk;
+  int ids[kPlanPerThread];
+#pragma unroll
+  for (int r = 0; r < kPlanPerThread; ++r) {
+    const int64_t f = base + r * kPlanThreads + tid;
+    const int v = f < n_pairs ? idx[f] : E;
+    ids[r] = (unsigned)v < (unsigned)E ? v : E;
+  }
   const int32_t *hb = a.hist + (int64_t)chunk * (E + 1);
   for (int e = tid; e < E; e += kPlanThreads) {
     run[e] = a.expert_off[e] + hb[e];
@@ -174,14 +198,10 @@ __device__ __forceinline__ void plan_rank_chunk(const MoeArgs &a, const int32_t 
 
   // id bits to compare: ids are in [0, E], E itself marking an invalid pair
   const int nbits = 32 - __clz(E);
-  const int64_t base = (int64_t)chunk * kPlanChunk;
+#pragma unroll
   for (int r = 0; r < kPlanPerThread; ++r) {
     const int64_t f = base + r * kPlanThreads + tid;
-    int e = E;
-    if (f < n_pairs) {
-      const int v = idx[f];
-      if ((unsigned)v < (unsigned)E) e = v;
-    }
+    const int e = ids[r];
     // lanes of this wavefront holding the same id
     uint64_t same = ~0ull;
     for (int b = 0; b < nbits; ++b) {
