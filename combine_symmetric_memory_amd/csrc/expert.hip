@@ -114,8 +114,25 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   // turn (the tiles still left there at the end): the XCDs finish together
   // whatever their ranges cost.  A unit is the same work on any XCD, so
   // the result does not depend on who takes it.
+  // counters of every range, read once this workgroup's own range is done:
+  // a range already exhausted then is skipped without an atomic of its own
+  // (counters only grow during a launch)
+  int32_t seen[kNumXcd];
+#pragma unroll
+  for (int q = 0; q < kNumXcd; ++q) seen[q] = 0;
   for (int d = 0; d < kNumXcd; ++d) {
   const int rx = (xcd + d) % kNumXcd;  // the range's XCD
+  if (d == 1) {
+    __syncthreads();  // every thread has read the last unit
+    if (tid < kNumXcd)
+      scratch[4 + tid] = __hip_atomic_load(&g.queue[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kNumXcd; ++q) seen[q] = uniform(scratch[4 + q]);
+  }
+  int seen_rx = 0;
+#pragma unroll
+  for (int q = 0; q < kNumXcd; ++q) seen_rx = q == rx ? seen[q] : seen_rx;
   const int t_begin = (int)((int64_t)total * rx / kNumXcd);
   const int t_end = (int)((int64_t)total * (rx + 1) / kNumXcd);
 
@@ -134,6 +151,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   if (P < 2) P = 1;
   const int n_whole = P > 1 ? U - R : U;
   const int n_units = TAIL ? (P > 1 ? R * P : 0) : n_whole;
+  if (d > 0 && seen_rx >= n_units) continue;
 
   for (;;) {
     __syncthreads();  // every thread has read the previous unit
@@ -285,7 +303,10 @@ template <bool SWIGLU, bool A8 = false>
 hipError_t launch_gemm(const MoeArgs &a, GemmDesc g, int32_t T, int num_cus, hipStream_t st) {
   const int nwg = gemm_workgroups(num_cus);
   const int64_t min_tiles = (int64_t)g.ntiles * T * a.K / kBM;
-  g.allow_split = min_tiles < (int64_t)kSplitMaxRounds * nwg;
+  // a tile is cut into at least two ranges of kMinSplitSteps K-steps, so a
+  // shorter K never splits
+  g.allow_split = min_tiles < (int64_t)kSplitMaxRounds * nwg &&
+                  g.kdim / kBK >= 2 * kMinSplitSteps;
   hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, false, A8>), dim3(nwg), dim3(kGemmWaves * kWave),
                      kGemmLds, st, a, g);
   hipError_t err = hipGetLastError();
