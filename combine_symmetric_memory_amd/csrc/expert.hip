@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   // a range already exhausted then is skipped without an atomic of its own
   // (counters only grow during a launch)
   int32_t seen[kNumXcd];
+  int32_t ahead = -1;  // thread 0: a unit of the current range claimed ahead
 #pragma unroll
   for (int q = 0; q < kNumXcd; ++q) seen[q] = 0;
   for (int d = 0; d < kNumXcd; ++d) {
@@ -155,7 +156,9 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
 
   for (;;) {
     __syncthreads();  // every thread has read the previous unit
-    if (tid == 0) scratch[0] = atomicAdd(&g.queue[rx], 1);
+    // the unit claimed during the previous tile of this range, if any
+    if (tid == 0) scratch[0] = ahead >= 0 ? ahead : atomicAdd(&g.queue[rx], 1);
+    ahead = -1;
     __syncthreads();
     // the unit and everything derived from it are wavefront-uniform: keep
     // them in scalar registers, so that per-K-step offsets stay scalar
@@ -198,12 +201,22 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
         d[6] = rx * W + v;  // workspace slot of the first range
       }
     }
+    // the next unit of this range is claimed once the K loop is done, and
+    // read after the epilogue
+    // (the offset is an opaque zero: with a visibly uniform address the
+    // compiler would fold the lane's result right after the atomic and wait
+    // for it there)
+    auto claim_ahead = [&]() __attribute__((always_inline)) {
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      if (tid == 0) ahead = atomicAdd(&g.queue[rx] + z, 1);
+    };
     if (kind == 2)
-      run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU, kBK, A8>(a, g, smem, e, n_tile, row0,
-                                                               rows_valid, kb, nkt, part);
+      run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU, kBK, A8>(
+          a, g, smem, e, n_tile, row0, rows_valid, kb, nkt, part, claim_ahead);
     else
       run_tile<kBM, kBN, kStages, SWIGLU, kBK, A8>(a, g, smem, e, n_tile, row0, rows_valid, kb,
-                                                   nkt, part);
+                                                   nkt, part, claim_ahead);
   }
   }
   // the last workgroup out has seen every counter exhausted: rearm them for

@@ -279,11 +279,18 @@ static_assert(kBM * kBN == kSplitTileFloats && (kBM / 2) * (2 * kBN) == kSplitTi
 // With part == nullptr the result goes to the expert's output rows;
 // otherwise the fp32 sums of this K-range are written to part, row-major
 // [BM][BN] in the accumulators' column order.  Every wavefront of the
-// workgroup calls this with the same arguments.
-template <int BM, int BN, int STAGES, bool SWIGLU, int BK = kBK, bool A8 = false>
+// workgroup calls this with the same arguments.  after_kloop() runs once
+// the K loop's loads have all landed, before the results are written (the
+// caller issues the next tile's hand-out there, so that its round trip
+// overlaps the epilogue).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <int BM, int BN, int STAGES, bool SWIGLU, int BK = kBK, bool A8 = false,
+          class Hook = NoHook>
 __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, char *smem, int e,
                                          int n_tile, int row0, int rows_valid, int kb, int nkt,
-                                         float *part) {
+                                         float *part, Hook after_kloop = Hook{}) {
   constexpr int NW = kGemmWaves;
   constexpr int WM = BM / 128;          // wavefront rows
   constexpr int WN = NW / WM;           // wavefront columns
@@ -849,6 +856,7 @@ __device__ __forceinline__ void run_tile(const MoeArgs &a, const GemmDesc &g, ch
     wait_vmcnt<0>();  // the tail's re-loads land before the ring is reused
     // every wavefront is done with the LDS before the next tile refills it
     __syncthreads();
+    after_kloop();
 
     // The MFMAs take the weights as their first operand, so each 32x32
     // block holds the tile transposed: lane holds output row (lane % 32) of
