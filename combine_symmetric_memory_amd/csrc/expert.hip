@@ -114,9 +114,10 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   // turn (the tiles still left there at the end): the XCDs finish together
   // whatever their ranges cost.  A unit is the same work on any XCD, so
   // the result does not depend on who takes it.
-  // counters of every range, read once this workgroup's own range is done:
-  // a range already exhausted then is skipped without an atomic of its own
-  // (counters only grow during a launch)
+  //
+  // seen[]: the counters of every range, read once this workgroup's own
+  // range is done; a range already exhausted then is skipped without an
+  // atomic of its own (counters only grow during a launch).
   int32_t seen[kNumXcd];
   int32_t ahead = -1;  // thread 0: a unit of the current range claimed ahead
 #pragma unroll
@@ -201,11 +202,11 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
         d[6] = rx * W + v;  // workspace slot of the first range
       }
     }
-    // the next unit of this range is claimed once the K loop is done, and
-    // read after the epilogue
-    // (the offset is an opaque zero: with a visibly uniform address the
-    // compiler would fold the lane's result right after the atomic and wait
-    // for it there)
+    // The next unit of this range is claimed once the K loop is done and
+    // read after the epilogue, so the atomic's round trip overlaps the
+    // epilogue.  Its address offset is an opaque zero: with a visibly
+    // uniform address the compiler would derive the lane's result right
+    // after the atomic and wait for it there.
     auto claim_ahead = [&]() __attribute__((always_inline)) {
       int z = 0;
       asm volatile("" : "+v"(z));
