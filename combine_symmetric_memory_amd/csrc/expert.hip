@@ -108,7 +108,11 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
   // tiles run longer), so a workgroup whose range is exhausted takes tiles
   // from the others' counters.
   const int xcd = blockIdx.x % kNumXcd;
-  const int nk = g.kdim / kBK;
+  // K-step and ring depths of this instantiation: the 8-bit rows always
+  // take K-steps of 64 (whatever the build's K-step for bf16 rows)
+  constexpr int BKI = A8 ? 64 : kBK;
+  constexpr int SF = A8 ? 5 : kStages, SH = A8 ? 2 : kStagesHalf;
+  const int nk = g.kdim / BKI;
   const int W = gridDim.x / kNumXcd;
   // own range first; then, once it is exhausted, the other XCDs' ranges in
   // turn (the tiles still left there at the end): the XCDs finish together
@@ -213,10 +217,10 @@ __global__ __launch_bounds__(kGemmWaves * kWave) void grouped_gemm_kernel(MoeArg
       if (tid == 0) ahead = atomicAdd(&g.queue[rx] + z, 1);
     };
     if (kind == 2)
-      run_tile<kBM / 2, 2 * kBN, kStagesHalf, SWIGLU, kBK, A8>(
+      run_tile<kBM / 2, 2 * kBN, SH, SWIGLU, BKI, A8>(
           a, g, smem, e, n_tile, row0, rows_valid, kb, nkt, part, claim_ahead);
     else
-      run_tile<kBM, kBN, kStages, SWIGLU, kBK, A8>(a, g, smem, e, n_tile, row0, rows_valid, kb,
+      run_tile<kBM, kBN, SF, SWIGLU, BKI, A8>(a, g, smem, e, n_tile, row0, rows_valid, kb,
                                                    nkt, part, claim_ahead);
   }
   }
@@ -306,8 +310,10 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(MoeArgs a, GemmDesc g)
 }
 
 constexpr size_t kGemmLds =
-    std::max((size_t)ring_bytes(kBM, kBN, kStages, kBK),
-             (size_t)ring_bytes(kBM / 2, 2 * kBN, kStagesHalf, kBK));
+    std::max(std::max((size_t)ring_bytes(kBM, kBN, kStages, kBK),
+                      (size_t)ring_bytes(kBM / 2, 2 * kBN, kStagesHalf, kBK)),
+             std::max((size_t)ring_bytes(kBM, kBN, 5, 64, true),
+                      (size_t)ring_bytes(kBM / 2, 2 * kBN, 2, 64, true)));
 
 // The tail and fixup launches follow only when the GEMM may split, that is
 // when it can have fewer than kSplitMaxRounds rounds: every expert's rows R
@@ -320,7 +326,7 @@ hipError_t launch_gemm(const MoeArgs &a, GemmDesc g, int32_t T, int num_cus, hip
   // a tile is cut into at least two ranges of kMinSplitSteps K-steps, so a
   // shorter K never splits
   g.allow_split = min_tiles < (int64_t)kSplitMaxRounds * nwg &&
-                  g.kdim / kBK >= 2 * kMinSplitSteps;
+                  g.kdim / (A8 ? 64 : kBK) >= 2 * kMinSplitSteps;
   hipLaunchKernelGGL((grouped_gemm_kernel<SWIGLU, false, A8>), dim3(nwg), dim3(kGemmWaves * kWave),
                      kGemmLds, st, a, g);
   hipError_t err = hipGetLastError();
@@ -353,7 +359,7 @@ hipError_t launch_expert_gate_up(const MoeArgs &a, const uint16_t *w13, int32_t 
   g.a8_ns = a8_ns;
   g.a8_kshift = 0;
   if (a8_ns > 0)
-    while ((kBK << g.a8_kshift) < a.H / a8_ns) ++g.a8_kshift;
+    while ((64 << g.a8_kshift) < a.H / a8_ns) ++g.a8_kshift;
   return launch_gemm<true, true>(a, g, T, num_cus, st);
 }
 
