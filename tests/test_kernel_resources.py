@@ -14,11 +14,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "combine_symmetric_memory_amd", "csrc")
 
 
-def _usage(src):
+def _usage(src, defines=()):
     from combine_symmetric_memory_amd.build import HIPCC_FLAGS, hipcc
     out = os.path.join("/tmp", "cco_res_%d.o" % os.getpid())
-    r = subprocess.run([hipcc(), *HIPCC_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src),
-                        "-o", out, "-Rpass-analysis=kernel-resource-usage"],
+    r = subprocess.run([hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-x", "hip", "-c",
+                        os.path.join(CSRC, src), "-o", out, "-Rpass-analysis=kernel-resource-usage"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     kernels = {}
@@ -65,3 +65,16 @@ def test_gemm_mfma_loops_touch_no_scratch():
     assert hot, "no MFMA loop found"
     for b in hot:
         assert "scratch_" not in b, "scratch access inside an MFMA loop:\n" + b[:400]
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_switched_off_single_launch_kernel_still_builds():
+    # The single-launch kernel is left out of the library (its entry point
+    # reports CCO_ERR_DISABLED) but shares its device code with the other
+    # kernels; it must keep compiling against them, without scratch.
+    ks = _usage("fused.hip", defines=("CCO_BUILD_FUSED",))
+    fused = {n: u for n, u in ks.items() if "fused_kernel" in n}
+    assert len(fused) == 3, sorted(ks)
+    for name, u in fused.items():
+        assert u.get("ScratchSize", 0) == 0, "%s uses scratch: %s" % (name, u)
