@@ -348,3 +348,48 @@ def test_expert_8bit_mixtral_full_size(ccm, orc):
     assert torch.equal(out8.view(torch.int16), outb.view(torch.int16))
     say("  whole path bit-identical to the bf16 path")
     heap.destroy()
+
+
+def test_expert_8bit_decode_full_size(ccm, orc):
+    # the decode shape (T = 256, H = 7168, top-8 of 256 experts over 8
+    # slots, I = 2048): every expert holds a few rows, all of them in
+    # 128 x 512 remainder tiles, and both GEMMs cut their one short round
+    # into K-ranges.  The first and last row of every expert against the
+    # oracle, and the whole path bit-identical to the bf16 path on the
+    # oracle's dequantized tokens
+    cfg = get_config("decode")
+    say("case: 8-bit expert decode full size")
+    x8, sc, idx, w = _inputs(cfg, 128)
+    ns = sc.shape[1]
+    heap, moe = make_moe(cfg)
+    w13, w2 = expert_weights(cfg, "cuda")
+    out8, code = _run_fp8(moe, x8, sc, idx, w, w13, w2)
+    assert code == ccm.CCO_OK and moe.status()[0] == ccm.CCO_OK
+    ref = orc.plan(idx, cfg.E, cfg.S, moe.cap)
+    tot = moe.read_routing()[3]
+    w13h, w2h = bf16_bits(w13), bf16_bits(w2)
+
+    def one(e):
+        s, o, c = e // cfg.eps, int(ref.expert_off[e]), int(ref.counts[e])
+        rows = sorted({0, c - 1})
+        X = np.concatenate([orc.dequant_e4m3_rows(_read_rows8(moe, s, o + r, 1), ns)
+                            for r in rows])
+        Y = np.stack([moe.read_rows("out_tok", s, o + r, 1)[0] for r in rows])
+        return Y, orc.swiglu_rows(X, w13h[e], w2h[e], nthreads=2)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(one, [int(e) for e in np.nonzero(ref.counts)[0]]))
+    Y = np.concatenate([r[0] for r in res])
+    say("  %d experts, %d sampled rows" % (len(res), len(Y)))
+    assert_close(Y, np.concatenate([r[1] for r in res]), "expert rows (sampled)")
+    ot8 = [moe.read_rows("out_tok", s, 0, int(tot[s])) for s in range(cfg.S)]
+    xb = torch.from_numpy(orc.dequant_e4m3_rows(_token_rows(x8, sc), ns).view(np.int16)) \
+        .view(torch.bfloat16).cuda()
+    outb, code = _run_bf16(moe, xb, idx, w, w13, w2)
+    assert code == ccm.CCO_OK
+    for s in range(cfg.S):
+        np.testing.assert_array_equal(ot8[s], moe.read_rows("out_tok", s, 0, int(tot[s])),
+                                      err_msg="expert rows slot %d" % s)
+    assert torch.equal(out8.view(torch.int16), outb.view(torch.int16))
+    say("  whole path bit-identical to the bf16 path")
+    heap.destroy()
