@@ -222,8 +222,9 @@ int cco_moe_dispatch_fp8(cco_moe *m, const uint8_t *x8, const float *scales, int
  *   w2   device bf16 [E][H][I], 16-byte aligned
  * (both K-contiguous, like nn.Linear.weight).  Row counts are read on the
  * device; nothing is copied to the host.  Results are deterministic for a
- * given routing on a given device: in GEMMs of few tile rounds the last
- * tiles sum their K-steps in ranges, added in range order.  With
+ * given routing on a given device: in GEMMs of few tile rounds (and at
+ * least 16 K-steps of 64) the last tiles sum their K-steps in ranges,
+ * added in range order.  With
  * inter == 0 this is a no-op (identity experts; w13 and w2 may be NULL).
  * After cco_moe_dispatch_fp8 the rows X are the 8-bit receive rows, read in
  * place ([blog] "Zero-copy MoE dispatch", step 1: the received tokens come
@@ -247,9 +248,8 @@ int cco_moe_expert(cco_moe *m, const uint16_t *w13, const uint16_t *w2, void *st
  * cco_moe_dispatch_fp8: the same 2H-byte rows holding the 8-bit codes and
  * their scales, see there); rows [expert_off[e], expert_off[e] + counts[e])
  * belong to expert e, and the first slot_total[slot] rows are the ones
- * received.  Borrowed: valid until
- * the heap is destroyed, overwritten by the next dispatch.  NULL if slot is
- * out of range or m is NULL. */
+ * received.  Borrowed: valid until the heap is destroyed, overwritten by
+ * the next dispatch.  NULL if slot is out of range or m is NULL. */
 void *cco_moe_dispatch_view(cco_moe *m, int32_t slot);
 
 /* Combine staging window of `slot` ([blog] "Zero-copy MoE dispatch":
@@ -301,9 +301,8 @@ int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weig
  * other work holds some of the compute units), the status word becomes
  * CCO_ERR_TIMEOUT after about two seconds and the kernel exits.
  * Errors: CCO_ERR_INVALID_ARG (as the separate calls, and for top-k above
- * 8), CCO_ERR_HIP; device
- * errors as cco_moe_plan, plus CCO_ERR_TIMEOUT (all read by cco_moe_status).
- */
+ * 8), CCO_ERR_HIP; device errors as cco_moe_plan, plus CCO_ERR_TIMEOUT (all
+ * read by cco_moe_status). */
 int cco_moe_fused(cco_moe *m, const int32_t *topk_idx, const uint16_t *x, const float *weights,
                   const uint16_t *w13, const uint16_t *w2, uint16_t *out, int32_t T,
                   void *stream);
@@ -371,11 +370,11 @@ int cco_moe_plan_noalloc(const int32_t *topk_idx, int32_t T, int32_t K, int32_t 
 /* Per-kernel timing with HIP events on the launch stream.  While enabled,
  * each kernel launch of this object is bracketed by a pair of events; the
  * summary returns, per kernel kind, the number of timed launches and their
- * total milliseconds (kinds: 0 plan-count (the whole plan for a batch of
- * at most 2048 (token, k) pairs, which runs in one launch), 1 plan-rank, 2 dispatch,
- * 3 expert gate/up, 4 expert down, 5 combine, 6 combine copy-in,
- * 7 8-bit dispatch, 8 staging copy on the copy engines, 9 the single-launch
- * path of cco_moe_fused).
+ * total milliseconds.  Kinds: 0 plan-count (the whole plan for a batch of
+ * at most 2048 (token, k) pairs, which runs in one launch), 1 plan-rank,
+ * 2 dispatch, 3 expert gate/up, 4 expert down, 5 combine, 6 combine
+ * copy-in, 7 8-bit dispatch, 8 staging copy on the copy engines, 9 the
+ * single-launch path of cco_moe_fused.
  * Reading the summary synchronises the recorded events and resets it. */
 #define CCO_NUM_KERNEL_KINDS 10
 int cco_moe_set_timing(cco_moe *m, int enable);
