@@ -4,7 +4,9 @@ benchmark times.  Plan and dispatch are compared with the oracle in full
 rows (every m-tile kind: full, partial, the 128-row remainder tiles), and on
 one row of every 256-row m-tile where the GEMM splits its last tiles; combine
 on every token (bit-exact on the GPU's own expert rows, read slot by slot) and
-end to end on sampled tokens from x (within tolerance)."""
+end to end on sampled tokens from x (within tolerance).  Repeated runs of the
+full dsv3 batch, with a smaller batch in between, are bit-identical."""
+import dataclasses
 import gc
 from concurrent.futures import ThreadPoolExecutor
 
@@ -162,6 +164,41 @@ def test_dsv3_full(orc):
     tokens = np.random.default_rng(0).choice(cfg.T, size=24, replace=False)
     tokens = np.unique(np.concatenate([tokens, [0, cfg.T - 1]]))
     _end_to_end_tokens(orc, c, tokens[:8], got[tokens[:8]])
+    heap.destroy()
+
+
+def _window_digests(moe, S):
+    import hashlib
+    _, st, _ = moe.status()
+    d = []
+    for s in range(S):
+        for which in ("hbuf", "out_tok"):
+            rows = moe.read_rows(which, s, 0, int(st[s]))
+            d.append(hashlib.blake2b(rows.tobytes(), digest_size=16).hexdigest())
+    return d
+
+
+def test_dsv3_full_repeated_runs_are_bit_identical():
+    # the GEMMs' hand-out (per-XCD ranges, stealing, the next tile claimed
+    # during the epilogue) decides only who computes a tile: repeated runs of
+    # the full batch, with a smaller batch in between (which leaves the
+    # counters at other values), give the same bits in every window and in out
+    cfg = get_config("dsv3")
+    say("case: dsv3 full size, repeated runs", cfg)
+    c = make_case(cfg)
+    heap, moe = make_moe(cfg)
+    out0, code = run_path(moe, c)
+    assert code == 0
+    ref_out = bf16_bits(out0)
+    ref_win = _window_digests(moe, cfg.S)
+    small = dataclasses.replace(make_case(cfg, T=cfg.T // 2, weights=False), w13=c.w13, w2=c.w2)
+    for rep in range(2):
+        out_s, code = run_path(moe, small)
+        assert code == 0
+        out, code = run_path(moe, c)
+        assert code == 0 and moe.status()[0] == 0
+        np.testing.assert_array_equal(bf16_bits(out), ref_out, err_msg="run %d" % rep)
+        assert _window_digests(moe, cfg.S) == ref_win, "windows differ on run %d" % rep
     heap.destroy()
 
 
