@@ -61,7 +61,7 @@ typedef enum {
   CCO_ERR_HEAP_FULL = -6,      /* the heap's slots have no room for this object */
   CCO_ERR_TOO_LARGE = -7,      /* the batch exceeds the fixed scratch of cco_moe_plan_noalloc */
   CCO_ERR_TIMEOUT = -8,        /* device: a wait of cco_moe_fused gave up; outputs undefined */
-  CCO_ERR_DISABLED = -9        /* the entry point is switched off in this build */
+  CCO_ERR_DISABLED = -9        /* the entry point is switched off in the library */
 } cco_status;
 
 /* Opaque handles. */
@@ -277,9 +277,9 @@ void *cco_moe_combine_in_view(cco_moe *m, int32_t slot);
 int cco_moe_combine(cco_moe *m, const void *const *expert_out, const float *weights,
                     uint16_t *out, int32_t T, void *stream);
 
-/* SWITCHED OFF in this build: returns CCO_ERR_DISABLED before any launch
- * (its kernel faulted the GPU on its first run and the cause is not yet
- * shown).  The contract below is the one it is built to.
+/* SWITCHED OFF: returns CCO_ERR_DISABLED before any launch unless the
+ * library is compiled with CCO_BUILD_FUSED (its kernel faulted the GPU on
+ * its first run and the cause is not yet shown).  The contract below is the one it is built to.
  *
  * The whole path -- plan, dispatch, expert (SwiGLU gate/up and down),
  * combine -- in ONE persistent kernel launch ([blog] "Mega-MoE: mega-kernel
